@@ -1,0 +1,230 @@
+"""Benchmark of the context-parallel attention hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic inputs already resident in
+HBM:
+  * prefill (pass-KV) on rank 0's share of the 1M-token workload (S = 1048576,
+    cp = 8, 32 q / 8 kv heads, head_dim 128, bf16): the balanced split, the
+    8 ring steps (each a pointer select of the block of rank (0 - t) mod 8 and
+    one fused cpattn_ring_step_partial launch), and the merge / finalize;
+  * pass-Q decode (b = 8, kv_len = 1048576 in cp = 8 shards, same heads): the
+    per-shard partials and the three-quantity reduction;
+  * the byte / FLOP account of both.
+
+Printed: one JSON line. `value` is the prefill ring-step throughput in TFLOP/s
+(exact causal FLOPs of rank 0's 8 steps / time of those launches); the decode
+HBM throughput rides along under "decode". `roofline` covers the dominant
+kernel (the ring-step partial), timed with HIP events on the launch stream;
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill ring-step TFLOP/s (% MFMA peak); pass-Q decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline_prefill(w, rows=64):
+    """The oracle (fp64 numpy) on a bounded sample of the prefill metric's unit
+    of work: `rows` tail-chunk query rows of rank 0 x all 32 heads against the
+    full KV block of rank 7 (ring step 1, every key visible)."""
+    import oracle
+    import synth
+    S, cp, H, G, d = w.total_tokens, w.cp, w.n_hq, w.n_kv, w.head_dim
+    c = S // (2 * cp)
+    tail0 = (2 * cp - 1) * c
+    qs = synth.tensor_np(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, row_start=tail0, rows=rows)
+    # rank 7 holds chunks 7 and 8
+    kb = np.concatenate([synth.tensor_np(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype,
+                                         row_start=ch * c, rows=c) for ch in (7, 8)])
+    vb = np.concatenate([synth.tensor_np(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype,
+                                         row_start=ch * c, rows=c) for ch in (7, 8)])
+    n = kb.shape[0]
+    t0 = time.perf_counter()
+    oracle.partial_attention(qs, kb, vb, np.arange(rows), np.arange(n), None, w.softmax_scale, causal=False)
+    dt = time.perf_counter() - t0
+    flops = 4 * d * H * rows * n
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} tail-chunk query rows of rank 0 x {H} heads against rank 7's full KV block "
+                      f"({n} keys, ring step 1, no mask): {flops:.3e} flop in {dt:.2f} s (fp64 numpy)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (the cp ranks are emulated on it); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_attention_amd as ca
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ca.load()
+    dev = "cuda"
+    wp = synth.WORKLOADS["long"]
+    wd = synth.WORKLOADS["decode"]
+    S, cp, H, G, d = wp.total_tokens, wp.cp, wp.n_hq, wp.n_kv, wp.head_dim
+    cu = wp.cu_seqlens
+    rank = 0
+    c = S // (2 * cp)
+    rows = S // cp
+
+    # ---------------- inputs, generated on the device (not timed)
+    log("bench: generating prefill inputs")
+    pos0, _ = ca.balanced_split(cu, cp, rank)
+    q0 = torch.cat([synth.tensor_torch(wp.seed, synth.TENSOR_Q, (S, H, d), wp.scale_in, wp.dtype, dev,
+                                       row_start=int(pos0[0]), rows=c),
+                    synth.tensor_torch(wp.seed, synth.TENSOR_Q, (S, H, d), wp.scale_in, wp.dtype, dev,
+                                       row_start=int(pos0[c]), rows=c)])
+    kfull = synth.tensor_torch(wp.seed, synth.TENSOR_K, (S, G, d), wp.scale_in, wp.dtype, dev)
+    vfull = synth.tensor_torch(wp.seed, synth.TENSOR_V, (S, G, d), wp.scale_in, wp.dtype, dev)
+    blocks = []
+    for j in range(cp):
+        pj, _ = ca.balanced_split(cu, cp, j)
+        idx = torch.from_numpy(pj).to(dev)
+        blocks.append((kfull.index_select(0, idx).contiguous(), vfull.index_select(0, idx).contiguous()))
+    del kfull, vfull
+    acc = ca.new_partial(rows, H, d, dev)
+    out = torch.empty(rows, H, d, device=dev)
+    lse = torch.empty(rows, H, device=dev)
+    pdesc = ca.PrefillDesc(cp=cp, cu_seqlens=cu, n_hq=H, n_kv=G, head_dim=d, dtype=wp.dtype, scale=wp.softmax_scale)
+
+    log("bench: generating decode inputs")
+    b, Sd, dcp = wd.batch, wd.kv_len, wd.cp
+    n = Sd // dcp
+    qd = synth.tensor_torch(wd.seed, synth.TENSOR_Q, (b, H, d), wd.scale_in, wd.dtype, dev)
+    kshards, vshards = [], []
+    for tid, lst in ((synth.TENSOR_K, kshards), (synth.TENSOR_V, vshards)):
+        full = synth.tensor_torch(wd.seed, tid, (b * Sd, G, d), wd.scale_in, wd.dtype, dev).view(b, Sd, G, d)
+        for s in range(dcp):
+            lst.append(full[:, s * n:(s + 1) * n].contiguous())
+        del full
+    ddesc = ca.DecodeDesc(batch=b, cp=dcp, kv_len=Sd, n_hq=H, n_kv=G, head_dim=d, dtype=wd.dtype,
+                          scale=wd.softmax_scale)
+    sp = ca.new_partial(dcp * b, H, d, dev)
+    dout = torch.empty(b, H, d, device=dev)
+    dlse = torch.empty(b, H, device=dev)
+    ws = torch.empty(max(ca.passq_workspace_bytes(ddesc), 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    acc_p = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)
+    acc_d = ca.account(cp=dcp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, batch=b, kv_len=Sd)
+    stream = torch.cuda.current_stream()
+
+    def step(rec):
+        # A1 split (host) and A8 account are part of the step
+        ca.balanced_split(cu, cp, rank)
+        ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)
+        for t in range(cp):
+            j = (rank - t) % cp                 # A2: the block in hand at step t
+            if rec is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            ca.ring_step_partial(pdesc, rank, t, q0, blocks[j][0], blocks[j][1], acc, accumulate=t > 0)
+            if rec is not None:
+                e1 = torch.cuda.Event(enable_timing=True)
+                e1.record(stream)
+                rec["ring"].append((e0, e1, t))
+        ca.merge(acc, [], out=out, lse=lse)      # A4 finalize
+        if rec is not None:
+            e2 = torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+        ca.passq_decode(ddesc, qd, kshards, vshards, sp, dout, dlse, ws=ws)   # A5-A7
+        if rec is not None:
+            e3 = torch.cuda.Event(enable_timing=True)
+            e3.record(stream)
+            rec["decode"].append((e2, e3))
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    rec = {"ring": [], "decode": []}
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ring_ms = [a.elapsed_time(b_) for (a, b_, _) in rec["ring"]]
+    dec_ms = [a.elapsed_time(b_) for (a, b_) in rec["decode"]]
+    ring_flops = acc_p["rank_flops_exact"] * args.steps          # exact causal FLOPs of all timed ring launches
+    tflops = ring_flops / (sum(ring_ms) * 1e-3) / 1e12
+    per_launch_flops = acc_p["rank_flops_exact"] / cp
+    avg_launch_s = float(np.mean(ring_ms)) * 1e-3
+    achieved = per_launch_flops / avg_launch_s / 1e12
+    # decode algorithmic bytes: KV + q + shard triples + out/lse
+    dec_bytes = (acc_d["decode_kv_bytes_total"] + qd.numel() * 2 + dcp * b * H * (d + 2) * 4 + b * H * (d + 1) * 4)
+    dec_gbs = dec_bytes / (float(np.mean(dec_ms)) * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill: rank 0 share of S=1048576, cp=8 (2x65536 query rows x 8 ring-step KV blocks), "
+                        "32q/8kv heads, head_dim 128, bf16 inputs ~N(0,1)*0.5, fp32 accumulate; "
+                        "decode: b=8, kv_len=1048576 in cp=8 shards, 32q/8kv, head_dim 128, bf16",
+            "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "ring_launch_ms": [round(x, 3) for x in ring_ms[:cp]],
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "ring_step_mfma<128,4>",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "flops_per_launch": per_launch_flops, "avg_launch_ms": round(avg_launch_s * 1e3, 3),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1), "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "ms": round(float(np.mean(dec_ms)), 3), "bytes": dec_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        },
+    }
+    del blocks, kshards, vshards
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the CPU")
+        cb = cpu_baseline_prefill(wp)
+        cb.pop("seconds")
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,328 @@
+"""Python binding of libcpattn (context-parallel attention for MI355X).
+
+Argument marshalling only: every computation runs in the C library (host
+split / account) or its HIP kernels. torch tensors provide device memory and
+streams. The binding fails loudly when the library has not been built; there
+is no fallback path.
+
+Entry points mirror the C names of include/cpattn.h:
+    balanced_split, ring_step_partial, merge, passq_decode, account
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
+    "balanced_split", "ring_step_partial", "merge", "passq_decode", "passq_workspace_bytes",
+    "account", "new_partial",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libcpattn.so")
+
+OK, E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_OVERFLOW, E_WORKSPACE, E_DEVICE = range(7)
+_ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPPORTED",
+              4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
+DT_F32, DT_BF16 = 0, 1
+
+EXPORTS = ["cpattn_balanced_split", "cpattn_ring_step_partial", "cpattn_merge",
+           "cpattn_passq_decode", "cpattn_account", "cpattn_version"]
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_ERR_NAMES.get(code, code)}")
+
+
+# ------------------------------------------------------------------ C structs
+
+class _Partial(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("den", ctypes.c_void_p), ("num", ctypes.c_void_p)]
+
+
+class _PrefillDesc(ctypes.Structure):
+    _fields_ = [("cp", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)),
+                ("n_hq", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _DecodeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("cp", ctypes.c_int32), ("kv_len", ctypes.c_int64),
+                ("n_hq", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _AccountIn(ctypes.Structure):
+    _fields_ = [("cp", ctypes.c_int32), ("n_hq", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype_bytes", ctypes.c_int32),
+                ("c_kv", ctypes.c_int64), ("d_model", ctypes.c_int64), ("layers_local", ctypes.c_int64),
+                ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)), ("num_seqs", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("kv_len", ctypes.c_int64)]
+
+
+ACCOUNT_FIELDS = ["tokens_per_rank", "ring_steps", "p2p_ops", "passkv_bytes_per_step",
+                  "passkv_bytes_per_rank", "attn_flops", "step_flops", "rank_flops",
+                  "step0_flops_exact", "stepN_flops_exact", "rank_flops_exact", "kv_bytes_per_rank",
+                  "passq_dispatch_bytes", "passq_reduce_bytes", "decode_kv_bytes_per_rank",
+                  "decode_kv_bytes_total", "decode_flops"]
+
+
+class _AccountOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ACCOUNT_FIELDS]
+
+
+_lib = None
+
+
+def load():
+    """Loads libcpattn.so (built by context_attention_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"libcpattn.so is not built ({lib_path}); run "
+                           "`python -m context_attention_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.cpattn_balanced_split.argtypes = [ctypes.POINTER(ctypes.c_int64), i32, i32, i32,
+                                          ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.cpattn_ring_step_partial.argtypes = [ctypes.POINTER(_PrefillDesc), i32, i32, vp, vp, vp,
+                                             ctypes.POINTER(_Partial), i32, vp]
+    lib.cpattn_merge.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, ctypes.POINTER(_Partial),
+                                 vp, vp, vp]
+    lib.cpattn_passq_decode.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp,
+                                        ctypes.POINTER(ctypes.c_size_t), vp]
+    lib.cpattn_account.argtypes = [ctypes.POINTER(_AccountIn), ctypes.POINTER(_AccountOut)]
+    lib.cpattn_version.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        getattr(lib, name).restype = ctypes.c_char_p if name == "cpattn_version" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != OK:
+        raise CpattnError(rc, where)
+
+
+def _i64_array(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+def _i64_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+# ------------------------------------------------------------------ host entry points
+
+def balanced_split(cu_seqlens, cp: int, rank: int):
+    """cpattn_balanced_split: returns (positions int64 [S/cp], cu_local int64 [n+1])."""
+    lib = load()
+    cu = _i64_array(cu_seqlens)
+    n = cu.size - 1
+    total = int(cu[-1]) if cu.size else 0
+    pos = np.zeros(max(total // max(cp, 1), 1), dtype=np.int64)
+    cul = np.zeros(n + 1, dtype=np.int64)
+    _check(lib.cpattn_balanced_split(_i64_ptr(cu), n, cp, rank, _i64_ptr(pos), _i64_ptr(cul)),
+           "cpattn_balanced_split")
+    return pos[: total // cp], cul
+
+
+def account(*, cp: int, n_hq: int, n_kv: int, head_dim: int, dtype_bytes: int, cu_seqlens=None,
+            batch: int = 0, kv_len: int = 0, c_kv: int = 0, d_model: int = 0, layers_local: int = 1) -> dict:
+    """cpattn_account: the byte / FLOP / memory formulas as a dict of ints."""
+    lib = load()
+    a = _AccountIn(cp=cp, n_hq=n_hq, n_kv=n_kv, head_dim=head_dim, dtype_bytes=dtype_bytes,
+                   c_kv=c_kv, d_model=d_model, layers_local=layers_local, batch=batch, kv_len=kv_len)
+    keep = None
+    if cu_seqlens is not None:
+        keep = _i64_array(cu_seqlens)
+        a.cu_seqlens = _i64_ptr(keep)
+        a.num_seqs = keep.size - 1
+    out = _AccountOut()
+    _check(lib.cpattn_account(ctypes.byref(a), ctypes.byref(out)), "cpattn_account")
+    return {n: int(getattr(out, n)) for n in ACCOUNT_FIELDS}
+
+
+# ------------------------------------------------------------------ device entry points
+
+@dataclass
+class Partial:
+    """A device triple: m, den [rows, n_hq] and num [rows, n_hq, head_dim], fp32."""
+    m: "torch.Tensor"
+    den: "torch.Tensor"
+    num: "torch.Tensor"
+
+    def _c(self) -> _Partial:
+        for t in (self.m, self.den, self.num):
+            _dev_check(t, "float32")
+        return _Partial(self.m.data_ptr(), self.den.data_ptr(), self.num.data_ptr())
+
+
+def new_partial(rows: int, n_hq: int, head_dim: int, device="cuda") -> Partial:
+    import torch
+    return Partial(torch.empty(rows, n_hq, dtype=torch.float32, device=device),
+                   torch.empty(rows, n_hq, dtype=torch.float32, device=device),
+                   torch.empty(rows, n_hq, head_dim, dtype=torch.float32, device=device))
+
+
+@dataclass
+class PrefillDesc:
+    cp: int
+    cu_seqlens: Sequence[int]
+    n_hq: int
+    n_kv: int
+    head_dim: int
+    dtype: str       # 'bf16' or 'f32'
+    scale: float
+
+    def _c(self):
+        cu = _i64_array(self.cu_seqlens)
+        d = _PrefillDesc(cp=self.cp, num_seqs=cu.size - 1, cu_seqlens=_i64_ptr(cu), n_hq=self.n_hq,
+                         n_kv=self.n_kv, head_dim=self.head_dim, dtype=_dtype_code(self.dtype),
+                         scale=self.scale)
+        return d, cu
+
+
+@dataclass
+class DecodeDesc:
+    batch: int
+    cp: int
+    kv_len: int
+    n_hq: int
+    n_kv: int
+    head_dim: int
+    dtype: str
+    scale: float
+
+    def _c(self):
+        return _DecodeDesc(batch=self.batch, cp=self.cp, kv_len=self.kv_len, n_hq=self.n_hq, n_kv=self.n_kv,
+                           head_dim=self.head_dim, dtype=_dtype_code(self.dtype), scale=self.scale)
+
+
+def _dtype_code(name: str) -> int:
+    if name == "bf16":
+        return DT_BF16
+    if name == "f32":
+        return DT_F32
+    raise ValueError(f"dtype must be 'bf16' or 'f32', not {name!r}")
+
+
+_TORCH_DT = {"bf16": "bfloat16", "f32": "float32", "float32": "float32"}
+
+
+def _dev_check(t, dtype: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    if str(t.dtype) != "torch." + _TORCH_DT[dtype]:
+        raise ValueError(f"tensor dtype {t.dtype}, expected {_TORCH_DT[dtype]}")
+    if t.data_ptr() % 16:
+        raise ValueError("device tensor must be 16-byte aligned")
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def ring_step_partial(desc: PrefillDesc, rank: int, step: int, q_local, k_blk, v_blk, dst: Partial,
+                      accumulate: bool = False, stream=None) -> None:
+    """cpattn_ring_step_partial (see include/cpattn.h)."""
+    lib = load()
+    rows = int(np.asarray(desc.cu_seqlens)[-1]) // desc.cp
+    for t, h in ((q_local, desc.n_hq), (k_blk, desc.n_kv), (v_blk, desc.n_kv)):
+        _dev_check(t, desc.dtype)
+        if tuple(t.shape) != (rows, h, desc.head_dim):
+            raise ValueError(f"shape {tuple(t.shape)} != {(rows, h, desc.head_dim)}")
+    if tuple(dst.num.shape) != (rows, desc.n_hq, desc.head_dim) or tuple(dst.m.shape) != (rows, desc.n_hq) \
+            or tuple(dst.den.shape) != (rows, desc.n_hq):
+        raise ValueError("dst shape mismatch")
+    d, keep = desc._c()
+    p = dst._c()
+    _check(lib.cpattn_ring_step_partial(ctypes.byref(d), rank, step, q_local.data_ptr(), k_blk.data_ptr(),
+                                        v_blk.data_ptr(), ctypes.byref(p), int(bool(accumulate)),
+                                        _stream(stream)), "cpattn_ring_step_partial")
+
+
+def merge(acc: Partial, parts: Sequence[Partial] = (), out=None, lse=None, stream=None) -> None:
+    """cpattn_merge: acc = merge(acc, *parts); optionally out = num/den, lse = m + ln den."""
+    lib = load()
+    rows, n_hq, hd = acc.num.shape
+    for p in parts:
+        if p.num.shape != acc.num.shape or p.m.shape != acc.m.shape:
+            raise ValueError("part shape mismatch")
+    if out is not None:
+        _dev_check(out, "f32")
+        if tuple(out.shape) != (rows, n_hq, hd):
+            raise ValueError("out shape mismatch")
+    if lse is not None:
+        _dev_check(lse, "f32")
+        if tuple(lse.shape) != (rows, n_hq):
+            raise ValueError("lse shape mismatch")
+    arr = (_Partial * max(len(parts), 1))(*[p._c() for p in parts])
+    a = acc._c()
+    _check(lib.cpattn_merge(rows, n_hq, hd, arr if parts else None, len(parts), ctypes.byref(a),
+                            out.data_ptr() if out is not None else None,
+                            lse.data_ptr() if lse is not None else None, _stream(stream)), "cpattn_merge")
+
+
+def passq_workspace_bytes(desc: DecodeDesc) -> int:
+    lib = load()
+    d = desc._c()
+    n = ctypes.c_size_t(0)
+    _check(lib.cpattn_passq_decode(ctypes.byref(d), None, None, None, None, None, None, None,
+                                   ctypes.byref(n), None), "cpattn_passq_decode")
+    return int(n.value)
+
+
+def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, shard_partials: Partial,
+                 out, lse, ws=None, stream=None) -> None:
+    """cpattn_passq_decode (see include/cpattn.h). Allocates the workspace with
+    torch when `ws` is None."""
+    import torch
+    lib = load()
+    b, hq, hd = desc.batch, desc.n_hq, desc.head_dim
+    _dev_check(q, desc.dtype)
+    if tuple(q.shape) != (b, hq, hd):
+        raise ValueError("q shape mismatch")
+    if len(k_shards) != desc.cp or len(v_shards) != desc.cp:
+        raise ValueError("need cp K and V shards")
+    shard_len = desc.kv_len // desc.cp
+    for t in list(k_shards) + list(v_shards):
+        _dev_check(t, desc.dtype)
+        if tuple(t.shape) != (b, shard_len, desc.n_kv, hd):
+            raise ValueError(f"shard shape {tuple(t.shape)} != {(b, shard_len, desc.n_kv, hd)}")
+    if tuple(shard_partials.num.shape) != (desc.cp * b, hq, hd):
+        raise ValueError("shard_partials shape mismatch")
+    _dev_check(out, "f32")
+    _dev_check(lse, "f32")
+    need = passq_workspace_bytes(desc)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not ws.is_cuda or ws.data_ptr() % 16:
+        raise ValueError("workspace must be an aligned device tensor")
+    d = desc._c()
+    ks = (ctypes.c_void_p * desc.cp)(*[t.data_ptr() for t in k_shards])
+    vs = (ctypes.c_void_p * desc.cp)(*[t.data_ptr() for t in v_shards])
+    sp = shard_partials._c()
+    n = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check(lib.cpattn_passq_decode(ctypes.byref(d), q.data_ptr(), ks, vs, ctypes.byref(sp), out.data_ptr(),
+                                   lse.data_ptr(), ws.data_ptr(), ctypes.byref(n), _stream(stream)),
+           "cpattn_passq_decode")
+
+
+def version() -> str:
+    return load().cpattn_version().decode()

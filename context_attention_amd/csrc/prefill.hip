@@ -1,0 +1,583 @@
+// Pass-KV ring step: causal partial attention of one rank's rows over the KV
+// block of the rank (rank - step) mod cp, carrying the online-softmax triple
+// (G5 context-parallel modelling spec, Definitions table: "Pass-KV", "Ring
+// step", "Partial attention", "Balanced chunk split").
+//
+// Work geometry. Under the balanced split rank r holds chunk a_h = r (head) and
+// a_t = 2cp-1-r (tail) of every sequence; the block of rank j holds key chunks
+// b_h = j and b_t = 2cp-1-j. A (query chunk a, key chunk b) pair of the same
+// sequence is fully visible when b < a, a causal triangle when b == a (only at
+// step 0) and empty when b > a. Both kernels below walk, for their query rows,
+// only the key chunks that are not empty, and mask only the triangle and the
+// ragged end of a chunk.
+//
+// Kernels
+//   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 4 waves owns 32*4/HG
+//       query rows x HG query heads of one kv group; K and V tiles of 64 keys are
+//       staged in LDS and shared by the 4 waves. S^T = K Q^T and O^T = V^T P^T run
+//       on v_mfma_f32_32x32x16_bf16, so every lane owns one query column of both
+//       products and the softmax needs a single cross-lane exchange per tile.
+//   ring_step_generic<T, D>  fp32 (and bf16 head_dim 512): one workgroup per
+//       (query row, query head), fp32 arithmetic throughout.
+#include "kernels.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int kMaxSeq = 64;  // sequences per launch (the host splits larger batches)
+
+struct SeqTable {
+  int32_t n;                      // sequences in this launch
+  int32_t c[kMaxSeq];             // chunk length c_i = L_i / (2 cp)
+  int64_t row_off[kMaxSeq];       // first local row of sequence i (same in q and kv blocks)
+  int32_t start[kMaxSeq + 1];     // prefix of work units (tiles or rows) per sequence
+};
+
+struct StepArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  float *m;
+  float *den;
+  float *num;
+  int32_t n_hq;
+  int32_t n_kv;
+  int32_t a_head, a_tail;  // query chunk ids: rank, 2cp-1-rank
+  int32_t b_head, b_tail;  // key chunk ids: src, 2cp-1-src
+  float scale;             // softmax scale (natural units)
+  int32_t accumulate;
+};
+
+__device__ __forceinline__ int find_seq(const SeqTable &t, int32_t unit) {
+  int i = 0;
+  while (i + 1 < t.n && t.start[i + 1] <= unit) ++i;
+  return i;
+}
+
+// Writes one (row, head) triple; with accumulate, merges into what is there.
+// `num_vals` are this thread's elements at d indices given by the caller.
+__device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, float d_new) {
+  *mp = m_new;
+  *dp = d_new;
+}
+
+// ----------------------------------------------------------------------------
+// MFMA kernel (bf16)
+// ----------------------------------------------------------------------------
+
+constexpr int kBN = 64;        // keys per tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kVStride = kBN + 8;  // padded row of the transposed V tile (bf16 elements)
+
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  // 16-byte chunk permutation of a K row so that 16 lanes reading the same
+  // chunk of 16 consecutive rows hit 16 distinct bank groups.
+  return (D == 64) ? ((row >> 1) & 7) : (row & 15);
+}
+
+// Slot of tile key kk inside its 16-key group of the transposed V tile: the
+// order in which the MFMA k-index runs through the keys of the P fragment.
+__device__ __forceinline__ int v_slot_of_group(int kg) {
+  // group of 4 consecutive keys 4kg..4kg+3 -> first slot
+  return (kg >> 2) * 16 + (kg & 1) * 8 + ((kg >> 1) & 1) * 4;
+}
+
+template <int D, int HG>
+__global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, StepArgs a) {
+  constexpr int BM = 32 * kWaves / HG;          // query rows per workgroup
+  constexpr int KCH = D / 8;                    // 16-byte chunks per K row
+  constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
+  constexpr int DB = D / 32;                    // 32-wide d blocks of the output
+
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * kVStride];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int qi = lane & 31;
+  const int hf = lane >> 5;
+
+  const int n_hg = a.n_hq / HG;
+  const int unit = blockIdx.x / n_hg;
+  const int hg = blockIdx.x - unit * n_hg;
+  const int si = find_seq(tab, unit);
+  const int c = tab.c[si];
+  const int nt = (c + BM - 1) / BM;
+  int lt = unit - tab.start[si];
+  // tail-chunk tiles first (they see at least as many keys), each chunk in
+  // descending row order
+  const bool tail = lt < nt;
+  const int tile = tail ? (nt - 1 - lt) : (nt - 1 - (lt - nt));
+  const int qa = tail ? a.a_tail : a.a_head;
+  const int64_t qrow0 = tab.row_off[si] + (tail ? c : 0);   // first local row of this chunk
+
+  const int h = hg * HG + (wave % HG);
+  const int rep = a.n_hq / a.n_kv;
+  const int g = h / rep;
+  const int wrow0 = tile * BM + (wave / HG) * 32;           // wave's first row inside the chunk
+  const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
+
+  // key segments that are not empty
+  int nseg = 0;
+  int seg_b[2];
+  int64_t seg_row[2];
+  {
+    const int bh = a.b_head, bt = a.b_tail;
+    if (bt <= qa) { seg_b[nseg] = bt; seg_row[nseg] = tab.row_off[si] + c; ++nseg; }
+    if (bh <= qa) { seg_b[nseg] = bh; seg_row[nseg] = tab.row_off[si]; ++nseg; }
+  }
+
+  const int row = wrow0 + qi;
+  const bool row_ok = row < c;
+  const int64_t grow = qrow0 + row;   // local row index in the rank's buffer
+  float *mptr = a.m + (grow * a.n_hq + h);
+  float *dptr = a.den + (grow * a.n_hq + h);
+  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D;
+
+  if (nseg == 0) {
+    // every row of this tile sees no key: the identity (unchanged when accumulating)
+    if (!a.accumulate && row_ok) {
+      if (hf == 0) store_stats(mptr, dptr, kNegInf, 0.f);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = z;
+        }
+    }
+    return;
+  }
+
+  // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
+  const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
+  bf16x8_t qf[KS];
+  {
+    const __bf16 *qp = qbase + (grow * a.n_hq + h) * (int64_t)D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (row_ok) {
+        qf[ks] = *reinterpret_cast<const bf16x8_t *>(qp + ks * 16);
+      } else {
+        u32x4_t z = {0u, 0u, 0u, 0u};
+        qf[ks] = __builtin_bit_cast(bf16x8_t, z);
+      }
+    }
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run = kNegInf;   // running max of raw scores q.k
+  float l_run = 0.f;       // this lane's share of the denominator
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k);
+  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v);
+  const int64_t kv_stride = (int64_t)a.n_kv * D;   // elements between consecutive keys
+
+  for (int sg = 0; sg < nseg; ++sg) {
+    const bool diag = seg_b[sg] == qa;
+    const int kend = diag ? wg_row_end : c;         // keys [0, kend) of the chunk can be visible
+    const int64_t krow0 = seg_row[sg];
+    for (int k0 = 0; k0 < kend; k0 += kBN) {
+      __syncthreads();   // previous tile fully consumed
+      // ---- stage K (swizzled rows) and V (transposed, MFMA k-order) into LDS
+#pragma unroll
+      for (int i = 0; i < (kBN * KCH) / kThreads; ++i) {
+        const int x = tid + i * kThreads;
+        const int key = x / KCH;
+        const int ch = x - key * KCH;
+        u32x4_t val = {0u, 0u, 0u, 0u};
+        if (k0 + key < kend)
+          val = *reinterpret_cast<const u32x4_t *>(kbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
+        *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = val;
+      }
+      for (int x = tid; x < (kBN / 4) * KCH; x += kThreads) {
+        const int kg = x / KCH;
+        const int ch = x - kg * KCH;
+        u32x4_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kg * 4 + e;
+          w[e] = u32x4_t{0u, 0u, 0u, 0u};
+          if (k0 + key < kend)
+            w[e] = *reinterpret_cast<const u32x4_t *>(vbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
+        }
+        const int slot = v_slot_of_group(kg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // d = ch*8 + 2i (low halves) and d = ch*8 + 2i + 1 (high halves)
+          const uint32_t lo01 = (w[0][i] & 0xFFFFu) | (w[1][i] << 16);
+          const uint32_t lo23 = (w[2][i] & 0xFFFFu) | (w[3][i] << 16);
+          const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xFFFF0000u);
+          const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xFFFF0000u);
+          const int d0 = ch * 8 + 2 * i;
+          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<u32x2_t *>(&Vt[d0 * kVStride + slot]) = u32x2_t{lo01, lo23};
+          *reinterpret_cast<u32x2_t *>(&Vt[(d0 + 1) * kVStride + slot]) = u32x2_t{hi01, hi23};
+        }
+      }
+      __syncthreads();
+
+      // this wave's rows [wrow0, wrow0+32): tile fully in the future of all of them?
+      if (diag && k0 > wrow0 + 31) continue;
+      const bool need_mask = (k0 + kBN > kend) || (diag && k0 + kBN - 1 > wrow0);
+
+      // ---- S^T = K Q^T : two 32-key blocks
+      f32x16_t sacc[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
+        const int key = mb * 32 + qi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = ks * 2 + hf;
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
+          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
+        }
+      }
+
+      if (need_mask) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool vis = (kk < kend) && (!diag || kk <= row);
+            if (!vis) sacc[mb][r] = kNegInf;
+          }
+      }
+
+      // ---- online softmax (lane = query column; keys split over the two halves)
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new == kNegInf) continue;   // nothing visible for this query yet
+      const float alpha = exp2_fast((m_run - m_new) * sl2);
+      const float mref = m_new * sl2;
+      m_run = m_new;
+
+      uint32_t pk[2][8];
+      float psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
+          const float p1 = exp2_fast(fmaf(sacc[mb][r + 1], sl2, -mref));
+          psum += p0 + p1;
+          pk[mb][r >> 1] = pack_bf16x2(p0, p1);
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+      // ---- O^T += V^T P^T : 4 k-steps of 16 keys
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int mb = ks >> 1;
+        const int base = (ks & 1) * 4;
+        u32x4_t pw = {pk[mb][base], pk[mb][base + 1], pk[mb][base + 2], pk[mb][base + 3]};
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8_t vf =
+              *reinterpret_cast<const bf16x8_t *>(&Vt[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: natural-log max, full denominator, optional merge, store
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float m_nat = (m_run == kNegInf) ? kNegInf : m_run * a.scale;
+  float w_old = 0.f, w_new = 1.f, m_out = m_nat;
+  if (a.accumulate) {
+    const float m_old = *mptr;
+    merge_weights(m_old, m_nat, m_out, w_old, w_new);
+    const float d_old = *dptr;
+    const float d_out = w_old * d_old + w_new * l_tot;
+    if (hf == 0) store_stats(mptr, dptr, m_out, d_out);
+  } else {
+    if (hf == 0) store_stats(mptr, dptr, m_nat, l_tot);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
+      f32x4_t o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+      if (a.accumulate) {
+        const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
+        o = old * w_old + o * w_new;
+      }
+      *reinterpret_cast<f32x4_t *>(p) = o;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Generic kernel: one workgroup per (local row, query head), fp32 arithmetic.
+// ----------------------------------------------------------------------------
+
+constexpr int kGenThreads = 256;
+
+__device__ __forceinline__ float block_reduce_max(float v, float *scratch) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < kGenThreads / 64; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+
+__device__ __forceinline__ float block_reduce_sum(float v, float *scratch) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < kGenThreads / 64; ++i) r += scratch[i];
+  return r;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kGenThreads) void ring_step_generic(SeqTable tab, StepArgs a) {
+  constexpr int PER = (D + kGenThreads - 1) / kGenThreads;   // output elements per thread
+  __shared__ float qs[D];
+  __shared__ float pbuf[kGenThreads];
+  __shared__ float red[kGenThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;         // local row within this launch
+  const int h = blockIdx.y;
+  const int si = find_seq(tab, unit);
+  const int c = tab.c[si];
+  const int lr = unit - tab.start[si];         // 0 .. 2c-1
+  const bool tail = lr >= c;
+  const int qrow = tail ? lr - c : lr;         // row inside its chunk
+  const int qa = tail ? a.a_tail : a.a_head;
+  const int64_t grow = tab.row_off[si] + lr;
+  const int rep = a.n_hq / a.n_kv;
+  const int g = h / rep;
+
+  const T *qp = reinterpret_cast<const T *>(a.q) + (grow * a.n_hq + h) * (int64_t)D;
+  for (int d = tid; d < D; d += kGenThreads) qs[d] = Elem<T>::load1(qp + d);
+  __syncthreads();
+
+  const T *kb = reinterpret_cast<const T *>(a.k);
+  const T *vb = reinterpret_cast<const T *>(a.v);
+  const int64_t kv_stride = (int64_t)a.n_kv * D;
+
+  float m_run = kNegInf, l_run = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+
+  for (int sg = 0; sg < 2; ++sg) {
+    const int b = sg == 0 ? a.b_head : a.b_tail;
+    if (b > qa) continue;
+    const int kend = (b == qa) ? qrow + 1 : c;
+    const int64_t krow0 = tab.row_off[si] + (sg == 0 ? 0 : c);
+    for (int k0 = 0; k0 < kend; k0 += kGenThreads) {
+      const int key = k0 + tid;
+      float s = kNegInf;
+      if (key < kend) {
+        const T *kp = kb + (krow0 + key) * kv_stride + g * D;
+        float dot = 0.f;
+        for (int d = 0; d < D; d += 8) {
+          float kv8[8];
+          Elem<T>::load8(kp + d, kv8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot = fmaf(qs[d + e], kv8[e], dot);
+        }
+        s = dot * a.scale;
+      }
+      const float cmax = block_reduce_max(s, red);
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = (m_run == kNegInf) ? 0.f : expf(m_run - m_new);
+      const float p = (key < kend) ? expf(s - m_new) : 0.f;
+      pbuf[tid] = p;
+      const float psum = block_reduce_sum(p, red);   // its barriers also publish pbuf
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const int nk = min(kGenThreads, kend - k0);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int d = tid + i * kGenThreads;
+        if (d < D) {
+          float sum = 0.f;
+          const T *vp = vb + (krow0 + k0) * kv_stride + g * D + d;
+          for (int x = 0; x < nk; ++x) sum = fmaf(pbuf[x], Elem<T>::load1(vp + x * kv_stride), sum);
+          acc[i] = acc[i] * alpha + sum;
+        }
+      }
+      __syncthreads();   // pbuf is rewritten by the next chunk
+    }
+  }
+
+  float *mp = a.m + (grow * a.n_hq + h);
+  float *dp = a.den + (grow * a.n_hq + h);
+  float *np_ = a.num + (grow * a.n_hq + h) * (int64_t)D;
+  float w_old = 0.f, w_new = 1.f;
+  if (a.accumulate) {
+    float m_out;
+    merge_weights(*mp, m_run, m_out, w_old, w_new);
+    const float d_out = w_old * (*dp) + w_new * l_run;
+    __syncthreads();   // every thread has read m and den
+    if (tid == 0) store_stats(mp, dp, m_out, d_out);
+  } else if (tid == 0) {
+    store_stats(mp, dp, m_run, l_run);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = tid + i * kGenThreads;
+    if (d < D) np_[d] = a.accumulate ? (w_old * np_[d] + w_new * acc[i]) : acc[i];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+
+int pick_hg(int rep) { return (rep % 4 == 0) ? 4 : (rep % 2 == 0) ? 2 : 1; }
+
+template <int D, int HG>
+hipError_t launch_mfma(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
+  const int n_hg = a.n_hq / HG;
+  const int64_t blocks = (int64_t)units * n_hg;
+  hipLaunchKernelGGL((ring_step_mfma<D, HG>), dim3((unsigned)blocks), dim3(kThreads), 0, s, t, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_d(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
+  const int hg = pick_hg(a.n_hq / a.n_kv);
+  if (hg == 4) return launch_mfma<D, 4>(t, a, units, s);
+  if (hg == 2) return launch_mfma<D, 2>(t, a, units, s);
+  return launch_mfma<D, 1>(t, a, units, s);
+}
+
+template <typename T, int D>
+hipError_t launch_generic(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
+  hipLaunchKernelGGL((ring_step_generic<T, D>), dim3((unsigned)units, (unsigned)a.n_hq), dim3(kGenThreads), 0, s,
+                     t, a);
+  return hipGetLastError();
+}
+
+// The MFMA kernel covers bf16 with head_dim 64 and 128.
+bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || d == 128); }
+
+int rows_per_unit(int dtype, int d, int rep) {
+  return use_mfma(dtype, d) ? 32 * kWaves / pick_hg(rep) : 1;
+}
+
+hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
+  if (dtype == CPATTN_DT_BF16) {
+    if (d == 64) return launch_mfma_d<64>(t, a, units, s);
+    if (d == 128) return launch_mfma_d<128>(t, a, units, s);
+    return launch_generic<__bf16, 512>(t, a, units, s);
+  }
+  if (d == 64) return launch_generic<float, 64>(t, a, units, s);
+  if (d == 128) return launch_generic<float, 128>(t, a, units, s);
+  return launch_generic<float, 512>(t, a, units, s);
+}
+
+}  // namespace
+}  // namespace cpattn
+
+extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
+                                        const void *q_local, const void *k_blk, const void *v_blk,
+                                        const cpattn_partial *dst, int32_t accumulate, hipStream_t stream) {
+  using namespace cpattn;
+  if (desc == nullptr || dst == nullptr) return CPATTN_E_ARG;
+  const int cp = desc->cp;
+  if (cp < 1 || rank < 0 || rank >= cp || step < 0 || step >= cp) return CPATTN_E_ARG;
+  if (desc->num_seqs < 0 || (desc->num_seqs > 0 && desc->cu_seqlens == nullptr)) return CPATTN_E_ARG;
+  if (desc->n_hq < 1 || desc->n_kv < 1) return CPATTN_E_ARG;
+  if (desc->dtype != CPATTN_DT_F32 && desc->dtype != CPATTN_DT_BF16) return CPATTN_E_ARG;
+  if (accumulate != 0 && accumulate != 1) return CPATTN_E_ARG;
+  if (!(desc->scale > 0.f) || !(desc->scale < __builtin_huge_valf())) return CPATTN_E_ARG;
+  if (desc->n_hq % desc->n_kv != 0) return CPATTN_E_DIVISIBILITY;
+  const int d = desc->head_dim;
+  if (d != 64 && d != 128 && d != 512) return CPATTN_E_UNSUPPORTED;
+  if (desc->n_hq > 65535) return CPATTN_E_UNSUPPORTED;
+  const int64_t *cu = desc->cu_seqlens;
+  if (desc->num_seqs > 0 && cu[0] != 0) return CPATTN_E_ARG;
+  for (int i = 0; i < desc->num_seqs; ++i) {
+    const int64_t L = cu[i + 1] - cu[i];
+    if (L < 0) return CPATTN_E_ARG;
+    if (L % (2 * (int64_t)cp) != 0) return CPATTN_E_DIVISIBILITY;
+    if (L / (2 * cp) > (int64_t)1 << 30) return CPATTN_E_UNSUPPORTED;
+  }
+  const int64_t total = desc->num_seqs > 0 ? cu[desc->num_seqs] : 0;
+  if (total == 0) return CPATTN_OK;
+  if (q_local == nullptr || k_blk == nullptr || v_blk == nullptr || dst->m == nullptr || dst->den == nullptr ||
+      dst->num == nullptr)
+    return CPATTN_E_ARG;
+
+  const int src = ((rank - step) % cp + cp) % cp;
+  StepArgs a;
+  a.q = q_local;
+  a.k = k_blk;
+  a.v = v_blk;
+  a.m = dst->m;
+  a.den = dst->den;
+  a.num = dst->num;
+  a.n_hq = desc->n_hq;
+  a.n_kv = desc->n_kv;
+  a.a_head = rank;
+  a.a_tail = 2 * cp - 1 - rank;
+  a.b_head = src;
+  a.b_tail = 2 * cp - 1 - src;
+  a.scale = desc->scale;
+  a.accumulate = accumulate;
+
+  const int rep = desc->n_hq / desc->n_kv;
+  const int rpu = rows_per_unit(desc->dtype, d, rep);
+  const bool mfma = use_mfma(desc->dtype, d);
+  // group sequences into launches of at most kMaxSeq sequences and 2^31 blocks
+  int i = 0;
+  int64_t row_off = 0;
+  while (i < desc->num_seqs) {
+    SeqTable t;
+    t.n = 0;
+    t.start[0] = 0;
+    int64_t units = 0;
+    while (i < desc->num_seqs && t.n < kMaxSeq) {
+      const int64_t c = (cu[i + 1] - cu[i]) / (2 * cp);
+      const int64_t u = mfma ? 2 * ((c + rpu - 1) / rpu) : 2 * c;
+      const int64_t blocks_after = (units + u) * (mfma ? desc->n_hq / pick_hg(rep) : 1);
+      if (t.n > 0 && blocks_after > 0x7FFFFFFFLL) break;
+      if (blocks_after > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
+      t.c[t.n] = (int32_t)c;
+      t.row_off[t.n] = row_off;
+      units += u;
+      t.start[t.n + 1] = (int32_t)units;
+      row_off += 2 * c;
+      ++t.n;
+      ++i;
+    }
+    if (units == 0) continue;
+    const hipError_t e = launch(desc->dtype, d, t, a, (int)units, stream);
+    if (e != hipSuccess) return CPATTN_E_DEVICE;
+  }
+  return CPATTN_OK;
+}

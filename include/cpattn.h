@@ -1,0 +1,237 @@
+/*
+ * cpattn — context-parallel attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the G5 context-parallel modelling spec ("G5
+ * 上下文并行建模设计规格"): the balanced chunk split, the pass-KV ring step
+ * computing a causal partial attention that carries the online-softmax
+ * triple (max, numerator, denominator), the associative merge of triples,
+ * pass-Q decode (per-shard partials plus the reduction of the three
+ * quantities), and the byte / FLOP / memory formulas of its Formulas section.
+ * Sections cited below are sections of that page.
+ *
+ * Conventions shared by every entry point
+ *   - Return value: CPATTN_OK (0) or one of the CPATTN_E_* codes. Nothing is
+ *     thrown across this interface and nothing is printed. When a call
+ *     returns an error it has not written any output and has not enqueued
+ *     any GPU work (except CPATTN_E_DEVICE, raised when the runtime refuses
+ *     a launch that was already validated).
+ *   - The caller owns all memory. Host pointers are read during the call
+ *     only. Device pointers must stay valid until the work enqueued on the
+ *     given stream has finished; the library keeps no pointer after it
+ *     returns, allocates nothing and has no global state. Calls are
+ *     reentrant. Faults of enqueued kernels surface at the caller's next
+ *     synchronisation.
+ *   - There are no defaults: cp, scale and the shapes are explicit (the
+ *     spec's interface appendix: cp is an explicit positive integer, a
+ *     missing value is an error, never a silent default).
+ *   - Layouts are token-major and contiguous with head_dim innermost.
+ *     Device tensors must be 16-byte aligned.
+ *   - Supported head_dim: 64, 128, 512. Supported element types of Q, K, V:
+ *     fp32 and bf16. Partials, outputs and log-sum-exp are fp32.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_OK 0
+#define CPATTN_E_ARG 1          /* null pointer, negative size, rank/step out of range, bad enum */
+#define CPATTN_E_DIVISIBILITY 2 /* a length not divisible by 2*cp (prefill) or cp (decode),
+                                   or n_hq not a multiple of n_kv */
+#define CPATTN_E_UNSUPPORTED 3  /* head_dim or dtype without a kernel, shape past a kernel limit */
+#define CPATTN_E_OVERFLOW 4     /* an int64 result of cpattn_account would overflow */
+#define CPATTN_E_WORKSPACE 5    /* workspace smaller than the size cpattn_passq_decode asked for */
+#define CPATTN_E_DEVICE 6       /* the HIP runtime rejected a launch */
+
+typedef enum { CPATTN_DT_F32 = 0, CPATTN_DT_BF16 = 1 } cpattn_dtype;
+
+/* An online-softmax triple for `rows` x n_hq (row, head) pairs, all device fp32
+ * (Definitions table, "Partial attention"):
+ *   m   [rows, n_hq]        running max of the scaled scores, natural-log units
+ *   den [rows, n_hq]        sum of exp(s - m) over the keys seen
+ *   num [rows, n_hq, d_h]   sum of exp(s - m) * v over the keys seen (not normalised)
+ * A (row, head) that has seen no key is the merge identity: m = -inf, den = 0,
+ * num = 0. A triple is defined up to (m + x, e^-x den, e^-x num). */
+typedef struct {
+  float *m;
+  float *den;
+  float *num;
+} cpattn_partial;
+
+/* Prefill problem description.
+ *   cp          CP degree, >= 1.
+ *   num_seqs    number of packed sequences, >= 0.
+ *   cu_seqlens  HOST array [num_seqs + 1]: cu_seqlens[0] = 0, non-decreasing;
+ *               sequence i holds global packed tokens [cu[i], cu[i+1]). Every
+ *               length must be divisible by 2*cp (Definitions table, "Balanced
+ *               chunk split": 2*cp chunks per sequence).
+ *   n_hq, n_kv  query heads and key/value heads; q head h reads kv head
+ *               h / (n_hq / n_kv).
+ *   head_dim    64, 128 or 512.
+ *   dtype       element type of Q, K, V.
+ *   scale       softmax scale applied to q.k (e.g. 1/sqrt(head_dim)), > 0, finite. */
+typedef struct {
+  int32_t cp;
+  int32_t num_seqs;
+  const int64_t *cu_seqlens;
+  int32_t n_hq;
+  int32_t n_kv;
+  int32_t head_dim;
+  int32_t dtype;
+  float scale;
+} cpattn_prefill_desc;
+
+/* Decode problem description: `batch` queries of one token each, each against
+ * its own kv_len keys, split into cp contiguous shards of kv_len/cp keys. */
+typedef struct {
+  int32_t batch;
+  int32_t cp;
+  int64_t kv_len;
+  int32_t n_hq;
+  int32_t n_kv;
+  int32_t head_dim;
+  int32_t dtype;
+  float scale;
+} cpattn_decode_desc;
+
+/* Balanced chunk split (Definitions table, "Balanced chunk split"; Rationale).
+ * Host only. Each sequence i of length L_i is cut into 2*cp chunks of
+ * c_i = L_i / (2*cp) tokens; rank `rank` keeps chunk `rank` (head) and chunk
+ * 2*cp-1-rank (tail). Local order: sequence by sequence, head chunk then tail.
+ *   positions  out, HOST int64 [sum(L_i)/cp]: global packed token index of
+ *              every local row.
+ *   cu_local   out, HOST int64 [num_seqs + 1]: local cumulative lengths 2*c_i.
+ * Errors: E_ARG (null pointer, num_seqs < 0, rank outside [0, cp), cp < 1,
+ * decreasing cu_seqlens), E_DIVISIBILITY (L_i % (2*cp) != 0). */
+int cpattn_balanced_split(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t rank,
+                          int64_t *positions, int64_t *cu_local);
+
+/* One pass-KV ring step of one rank (Definitions table, "Pass-KV", "Ring step",
+ * "Partial attention"). Computes, for every local query row of rank `rank`
+ * and every query head, the causal partial attention over the KV block that
+ * rank (rank - step) mod cp holds:
+ *   visible keys: same sequence, global key position <= global query position;
+ *   triple over them as in cpattn_partial (rows that see no key: identity).
+ *   q_local  device [S/cp, n_hq, head_dim] rows of `rank`, in the local order of
+ *            cpattn_balanced_split (S = cu_seqlens[num_seqs]).
+ *   k_blk, v_blk  device [S/cp, n_kv, head_dim], the rows of rank (rank-step) mod cp
+ *            in that rank's local order.
+ *   dst      device triple for S/cp rows.
+ *   accumulate  0: dst = partial; 1: dst = merge(dst, partial) (dst must then hold
+ *            a valid triple, e.g. the previous step's result).
+ * bf16 inputs use MFMA with fp32 accumulation; fp32 inputs compute in fp32.
+ * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_DEVICE. */
+int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
+                             const void *q_local, const void *k_blk, const void *v_blk,
+                             const cpattn_partial *dst, int32_t accumulate, hipStream_t stream);
+
+/* Merge and finalize (Definitions table, "Partial attention": the merge is
+ * associative and order-independent).
+ *   acc   in/out device triple [rows, n_hq(, head_dim)]: acc = merge(acc, parts[0], ...,
+ *         parts[n_parts-1]) with m = max m_i, alpha_i = exp(m_i - m) (0 for m_i = -inf),
+ *         den = sum alpha_i den_i, num = sum alpha_i num_i.
+ *   parts HOST array of n_parts device triples of the same shape (n_parts >= 0;
+ *         parts may be NULL when n_parts == 0).
+ *   out   device fp32 [rows, n_hq, head_dim] or NULL: num / den (0 for identity rows).
+ *   lse   device fp32 [rows, n_hq] or NULL: m + ln(den) (-inf for identity rows).
+ * Errors: E_ARG, E_UNSUPPORTED, E_DEVICE. */
+int cpattn_merge(int64_t rows, int32_t n_hq, int32_t head_dim,
+                 const cpattn_partial *parts, int32_t n_parts, const cpattn_partial *acc,
+                 float *out, float *lse, hipStream_t stream);
+
+/* Pass-Q decode (Definitions table, "Pass-Q"; Use case, decode): the query is
+ * sent to every shard, shard s computes the partial triple over its kv_len/cp
+ * keys (no mask), and the cp shard triples are reduced into the result.
+ *   q         device [batch, n_hq, head_dim].
+ *   k_shards, v_shards  HOST arrays of cp device pointers, each [batch, kv_len/cp, n_kv, head_dim].
+ *   shard_partials  device triple with rows = cp*batch (shard-major: row s*batch + b):
+ *             the per-shard triples, written by this call.
+ *   out       device fp32 [batch, n_hq, head_dim];  lse device fp32 [batch, n_hq].
+ *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the
+ *             required size in *ws_bytes and returns CPATTN_OK. Otherwise *ws_bytes
+ *             is the size available (E_WORKSPACE if too small).
+ * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE. */
+int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q,
+                        const void *const *k_shards, const void *const *v_shards,
+                        const cpattn_partial *shard_partials, float *out, float *lse,
+                        void *ws, size_t *ws_bytes, hipStream_t stream);
+
+/* Inputs of cpattn_account. Prefill fields are used when cu_seqlens != NULL,
+ * decode fields when kv_len > 0.
+ *   cp, n_hq, n_kv, head_dim  as above; dtype_bytes = s, the model element size.
+ *   c_kv           K+V bytes per token per layer (Definitions table); 0 means
+ *                  2 * n_kv * head_dim * dtype_bytes.
+ *   d_model        d, the model hidden size (Definitions table); 0 means n_hq * head_dim.
+ *   layers_local   L_local of the memory formula, >= 1.
+ *   cu_seqlens, num_seqs  HOST, packed prefill lengths (b folded in), each % (2*cp) == 0.
+ *   batch, kv_len  decode batch b and KV length S (kv_len % cp == 0). */
+typedef struct {
+  int32_t cp;
+  int32_t n_hq;
+  int32_t n_kv;
+  int32_t head_dim;
+  int32_t dtype_bytes;
+  int64_t c_kv;
+  int64_t d_model;
+  int64_t layers_local;
+  const int64_t *cu_seqlens;
+  int32_t num_seqs;
+  int32_t batch;
+  int64_t kv_len;
+} cpattn_account_in;
+
+/* Formulas section; every field exact in int64. Fields of a part that was not
+ * requested are 0.
+ *   tokens_per_rank         S/cp
+ *   ring_steps, p2p_ops     cp compute steps and cp-1 transfers per rank and layer
+ *   passkv_bytes_per_step   S/cp * c_kv (0 at cp = 1)
+ *   passkv_bytes_per_rank   (cp-1) * S/cp * c_kv            (eq. g5cp-passkv-bytes)
+ *   attn_flops              F_attn = sum_i 2 * n_hq * head_dim * L_i^2
+ *   step_flops              F_attn / cp^2                   (eq. g5cp-step-flops)
+ *   rank_flops              F_attn / cp
+ *   step0_flops_exact       4 * head_dim * n_hq * sum_i (2 c_i^2 + c_i)   (inclusive diagonal)
+ *   stepN_flops_exact       4 * head_dim * n_hq * sum_i 2 c_i^2           (steps >= 1)
+ *   rank_flops_exact        step0 + (cp-1) * stepN
+ *   kv_bytes_per_rank       S * c_kv * L_local / cp          (prefill KV memory)
+ *   passq_dispatch_bytes    b * d * s   (0 at cp = 1)
+ *   passq_reduce_bytes      b * (d + 2 n_h) * s   (0 at cp = 1; n_h = n_hq)
+ *   decode_kv_bytes_per_rank  b * S * c_kv * L_local / cp
+ *   decode_kv_bytes_total   b * S * c_kv * L_local
+ *   decode_flops            4 * b * n_hq * head_dim * S */
+typedef struct {
+  int64_t tokens_per_rank;
+  int64_t ring_steps;
+  int64_t p2p_ops;
+  int64_t passkv_bytes_per_step;
+  int64_t passkv_bytes_per_rank;
+  int64_t attn_flops;
+  int64_t step_flops;
+  int64_t rank_flops;
+  int64_t step0_flops_exact;
+  int64_t stepN_flops_exact;
+  int64_t rank_flops_exact;
+  int64_t kv_bytes_per_rank;
+  int64_t passq_dispatch_bytes;
+  int64_t passq_reduce_bytes;
+  int64_t decode_kv_bytes_per_rank;
+  int64_t decode_kv_bytes_total;
+  int64_t decode_flops;
+} cpattn_account_out;
+
+/* Host only. Errors: E_ARG, E_DIVISIBILITY, E_OVERFLOW. */
+int cpattn_account(const cpattn_account_in *in, cpattn_account_out *out);
+
+/* Library version string (static storage). */
+const char *cpattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -71,6 +71,18 @@ def _mix_np(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def _unit_from_index(i: np.ndarray, k1: int, k2: int, k3: int) -> np.ndarray:
+    """Unit-variance fp32 values for an array of uint64 flat indices."""
+    hi = (i >> np.uint64(32)).astype(np.uint32)
+    lo = i.astype(np.uint32)            # low 32 bits
+    h1 = _mix_np(_mix_np(lo ^ np.uint32(k2)) ^ hi ^ np.uint32(k3))
+    h2 = _mix_np(h1 ^ np.uint32(k1))
+    m16 = np.uint32(0xFFFF)
+    u = ((h1 & m16).astype(np.int32) + (h1 >> np.uint32(16)).astype(np.int32)
+         + (h2 & m16).astype(np.int32) + (h2 >> np.uint32(16)).astype(np.int32))
+    return (u - 131070).astype(np.float32) * UNIT
+
+
 def unit_values_np(seed: int, tensor_id: int, start: int, count: int) -> np.ndarray:
     """fp32 unit-variance values for flat indices [start, start + count)."""
     k1, k2, k3 = _keys(seed, tensor_id)
@@ -78,17 +90,42 @@ def unit_values_np(seed: int, tensor_id: int, start: int, count: int) -> np.ndar
     step = 1 << 20
     for pos in range(0, count, step):
         n = min(step, count - pos)
-        a = start + pos
-        # low and high 32-bit words of the flat index; the low word may wrap inside a block
-        lo = np.arange(n, dtype=np.uint64) + np.uint64(a)
-        hi = (lo >> np.uint64(32)).astype(np.uint32)
-        lo = lo.astype(np.uint32)
-        h1 = _mix_np(_mix_np(lo ^ np.uint32(k2)) ^ hi ^ np.uint32(k3))
-        h2 = _mix_np(h1 ^ np.uint32(k1))
-        m16 = np.uint32(0xFFFF)
-        u = ((h1 & m16).astype(np.int32) + (h1 >> np.uint32(16)).astype(np.int32)
-             + (h2 & m16).astype(np.int32) + (h2 >> np.uint32(16)).astype(np.int32))
-        out[pos:pos + n] = (u - 131070).astype(np.float32) * UNIT
+        i = np.arange(n, dtype=np.uint64) + np.uint64(start + pos)
+        out[pos:pos + n] = _unit_from_index(i, k1, k2, k3)
+    return out
+
+
+def values_at_np(seed: int, tensor_id: int, index: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+    """Values at arbitrary flat indices (any shape); same numbers as values_np."""
+    k1, k2, k3 = _keys(seed, tensor_id)
+    idx = np.asarray(index, dtype=np.int64)
+    flat = idx.reshape(-1)
+    x = np.empty(flat.size, dtype=np.float32)
+    step = 1 << 20
+    for pos in range(0, flat.size, step):
+        x[pos:pos + step] = _unit_from_index(flat[pos:pos + step].astype(np.uint64), k1, k2, k3)
+    x = x * np.float32(scale)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x).reshape(idx.shape)
+    if dtype == "f32":
+        return x.reshape(idx.shape)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def head_slice_np(seed: int, tensor_id: int, shape: Sequence[int], head: int, scale: float, dtype: str,
+                  row_start: int = 0, rows: Optional[int] = None) -> np.ndarray:
+    """x[row_start:row_start+rows, head, :] of a synthetic [T, H, D] tensor, i.e.
+    one head of a token-major tensor, as [rows, 1, D]."""
+    T, H, D = (int(s) for s in shape)
+    if rows is None:
+        rows = T - row_start
+    out = np.empty((rows, 1, D), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    step = max(1, (1 << 20) // D)
+    d = np.arange(D, dtype=np.int64)
+    for r0 in range(0, rows, step):
+        r = np.arange(row_start + r0, row_start + min(rows, r0 + step), dtype=np.int64)
+        idx = (r[:, None] * H + head) * D + d[None, :]
+        out[r0:r0 + r.size, 0, :] = values_at_np(seed, tensor_id, idx, scale, dtype)
     return out
 
 

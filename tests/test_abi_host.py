@@ -1,0 +1,169 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and its host-only entry points (split, account, argument checks)
+match the oracle bit for bit. No GPU compute is called here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import context_attention_amd as ca
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ca.lib_path), reason="libcpattn.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(cpattn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(ca.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ca.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ca.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (cpattn_\w+)", out))
+    assert set(_declared()) <= exported
+    assert ca.version().startswith("cpattn")
+
+
+CASES = [([0, 8], 2), ([0, 16], 4), ([0, 256], 2), ([0, 32768], 8), ([0, 24, 48, 120], 3),
+         (list(np.concatenate([[0], np.cumsum([12464, 15568, 14688, 9376, 15536, 16048])])), 4),
+         ([0, 0, 16, 16], 4), ([0, 6, 10], 1)]
+
+
+@pytest.mark.parametrize("cu,cp", CASES)
+def test_split_matches_oracle(cu, cp):
+    for r in range(cp):
+        pos, cul = ca.balanced_split(cu, cp, r)
+        opos, ocul = oracle.balanced_split(cu, cp, r)
+        np.testing.assert_array_equal(pos, opos)
+        np.testing.assert_array_equal(cul, ocul)
+
+
+def test_split_errors():
+    with pytest.raises(ca.CpattnError) as e:
+        ca.balanced_split([0, 10], 2, 0)
+    assert e.value.code == ca.E_DIVISIBILITY
+    for cu, cp, r in (([0, 8], 0, 0), ([0, 8], 2, 2), ([0, 8], 2, -1), ([1, 8], 1, 0), ([0, 8, 4], 1, 0)):
+        with pytest.raises(ca.CpattnError) as e:
+            ca.balanced_split(cu, cp, r)
+        assert e.value.code == ca.E_ARG
+
+
+def test_split_untouched_on_error():
+    lib = ca.load()
+    cu = np.array([0, 10], dtype=np.int64)
+    pos = np.full(8, -7, dtype=np.int64)
+    cul = np.full(2, -7, dtype=np.int64)
+    rc = lib.cpattn_balanced_split(cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1, 2, 0,
+                                   pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   cul.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    assert rc == ca.E_DIVISIBILITY
+    assert np.all(pos == -7) and np.all(cul == -7)
+
+
+ACCOUNT_CASES = [
+    dict(cp=2, n_hq=2, n_kv=2, head_dim=64, dtype_bytes=4, cu_seqlens=[0, 256]),
+    dict(cp=8, n_hq=32, n_kv=8, head_dim=128, dtype_bytes=2, cu_seqlens=[0, 32768]),
+    dict(cp=8, n_hq=32, n_kv=8, head_dim=128, dtype_bytes=2, cu_seqlens=[0, 1 << 20]),
+    dict(cp=8, n_hq=32, n_kv=8, head_dim=128, dtype_bytes=2, batch=8, kv_len=1 << 20),
+    dict(cp=4, n_hq=64, n_kv=64, head_dim=512, dtype_bytes=2,
+         cu_seqlens=list(np.concatenate([[0], np.cumsum([12464, 15568, 14688, 9376, 15536, 16048])]))),
+    dict(cp=1, n_hq=8, n_kv=2, head_dim=128, dtype_bytes=2, cu_seqlens=[0, 100, 300], batch=3, kv_len=77),
+    dict(cp=3, n_hq=6, n_kv=3, head_dim=64, dtype_bytes=2, cu_seqlens=[0, 12, 12, 60], batch=2, kv_len=99,
+         layers_local=5, c_kv=320, d_model=7168),
+]
+
+
+@pytest.mark.parametrize("case", ACCOUNT_CASES)
+def test_account_matches_oracle(case):
+    got = ca.account(**case)
+    want = oracle.account(**{k: v for k, v in case.items() if k not in ("batch", "kv_len") or v},
+                          **({} if "kv_len" in case else {}))
+    for k, v in want.items():
+        assert got[k] == v, k
+    # fields of a part not requested are zero
+    if "kv_len" not in case:
+        assert got["decode_flops"] == 0 and got["passq_dispatch_bytes"] == 0
+    if "cu_seqlens" not in case:
+        assert got["attn_flops"] == 0 and got["tokens_per_rank"] == 0
+
+
+def test_account_errors():
+    base = dict(cp=2, n_hq=4, n_kv=2, head_dim=64, dtype_bytes=2, cu_seqlens=[0, 16])
+    for bad, code in ((dict(cp=0), ca.E_ARG), (dict(n_kv=3), ca.E_DIVISIBILITY),
+                      (dict(cu_seqlens=[0, 6]), ca.E_DIVISIBILITY), (dict(kv_len=7), ca.E_DIVISIBILITY),
+                      (dict(layers_local=0), ca.E_ARG), (dict(dtype_bytes=0), ca.E_ARG)):
+        with pytest.raises(ca.CpattnError) as e:
+            ca.account(**{**base, **bad})
+        assert e.value.code == code, bad
+    # int64 overflow is reported, not wrapped
+    with pytest.raises(ca.CpattnError) as e:
+        ca.account(cp=2, n_hq=1 << 20, n_kv=1, head_dim=512, dtype_bytes=8, cu_seqlens=[0, 1 << 40])
+    assert e.value.code == ca.E_OVERFLOW
+
+
+def test_device_entry_points_reject_bad_arguments_without_gpu():
+    """Argument validation runs before any device call, so it is testable on
+    the CPU; every rejected call returns its code."""
+    lib = ca.load()
+    cu = np.array([0, 16], dtype=np.int64)
+    P = ctypes.POINTER(ctypes.c_int64)
+
+    def desc(**kw):
+        d = dict(cp=2, num_seqs=1, cu_seqlens=cu.ctypes.data_as(P), n_hq=4, n_kv=2, head_dim=128,
+                 dtype=ca.DT_BF16, scale=0.125)
+        d.update(kw)
+        return ca._PrefillDesc(**d)
+
+    dummy = ctypes.c_void_p(16)
+    part = ca._Partial(16, 16, 16)
+    cases = [
+        (desc(cp=0), 0, 0, ca.E_ARG),
+        (desc(), 2, 0, ca.E_ARG),
+        (desc(), 0, -1, ca.E_ARG),
+        (desc(n_kv=3), 0, 0, ca.E_DIVISIBILITY),
+        (desc(head_dim=96), 0, 0, ca.E_UNSUPPORTED),
+        (desc(dtype=7), 0, 0, ca.E_ARG),
+        (desc(scale=0.0), 0, 0, ca.E_ARG),
+        (desc(scale=float("nan")), 0, 0, ca.E_ARG),
+    ]
+    cu_bad = np.array([0, 10], dtype=np.int64)
+    cases.append((desc(cu_seqlens=cu_bad.ctypes.data_as(P)), 0, 0, ca.E_DIVISIBILITY))
+    for d, r, s, code in cases:
+        assert lib.cpattn_ring_step_partial(ctypes.byref(d), r, s, dummy, dummy, dummy, ctypes.byref(part),
+                                            0, None) == code
+    # null destination
+    assert lib.cpattn_ring_step_partial(ctypes.byref(desc()), 0, 0, dummy, dummy, dummy, None, 0, None) == ca.E_ARG
+    # merge
+    assert lib.cpattn_merge(4, 2, 96, None, 0, ctypes.byref(part), None, None, None) == ca.E_UNSUPPORTED
+    assert lib.cpattn_merge(-1, 2, 64, None, 0, ctypes.byref(part), None, None, None) == ca.E_ARG
+    assert lib.cpattn_merge(4, 2, 64, None, 1, ctypes.byref(part), None, None, None) == ca.E_ARG
+    # decode: size query and validation
+    dd = ca._DecodeDesc(batch=8, cp=8, kv_len=1 << 20, n_hq=32, n_kv=8, head_dim=128, dtype=ca.DT_BF16,
+                        scale=0.088)
+    n = ctypes.c_size_t(0)
+    assert lib.cpattn_passq_decode(ctypes.byref(dd), None, None, None, None, None, None, None,
+                                   ctypes.byref(n), None) == ca.OK
+    assert n.value > 0
+    small = ctypes.c_size_t(n.value - 4)
+    assert lib.cpattn_passq_decode(ctypes.byref(dd), dummy, None, None, None, None, None, dummy,
+                                   ctypes.byref(small), None) == ca.E_WORKSPACE
+    bad = ca._DecodeDesc(batch=8, cp=3, kv_len=100, n_hq=32, n_kv=8, head_dim=128, dtype=ca.DT_BF16, scale=0.1)
+    assert lib.cpattn_passq_decode(ctypes.byref(bad), None, None, None, None, None, None, None,
+                                   ctypes.byref(n), None) == ca.E_DIVISIBILITY
+    bad = ca._DecodeDesc(batch=8, cp=8, kv_len=1 << 20, n_hq=24, n_kv=8, head_dim=128, dtype=ca.DT_BF16,
+                         scale=0.1)
+    assert lib.cpattn_passq_decode(ctypes.byref(bad), None, None, None, None, None, None, None,
+                                   ctypes.byref(n), None) == ca.E_UNSUPPORTED

@@ -38,3 +38,11 @@ def test_row_slices_consistent():
     full = synth.tensor_np(3, 1, (10, 2, 4), 0.5, "bf16")
     part = synth.tensor_np(3, 1, (10, 2, 4), 0.5, "bf16", row_start=3, rows=4)
     np.testing.assert_array_equal(full[3:7], part)
+
+
+def test_values_at_and_head_slice():
+    full = synth.tensor_np(4, 2, (50, 3, 8), 0.5, "bf16")
+    np.testing.assert_array_equal(synth.head_slice_np(4, 2, (50, 3, 8), 1, 0.5, "bf16"), full[:, 1:2, :])
+    np.testing.assert_array_equal(synth.head_slice_np(4, 2, (50, 3, 8), 2, 0.5, "bf16", 7, 20), full[7:27, 2:3])
+    idx = np.array([[5, 900], [1199, 0]])
+    np.testing.assert_array_equal(synth.values_at_np(4, 2, idx, 0.5, "bf16"), full.reshape(-1)[idx])
