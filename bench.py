@@ -38,10 +38,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline_prefill(w, rows=64):
+def cpu_baseline_prefill(w, rows=64, target_s=15.0):
     """The oracle (fp64 numpy) on a bounded sample of the prefill metric's unit
-    of work: `rows` tail-chunk query rows of rank 0 x all 32 heads against the
-    full KV block of rank 7 (ring step 1, every key visible)."""
+    of work: tail-chunk query rows of rank 0 x all 32 heads against the full KV
+    block of rank 7 (ring step 1, every key visible). A first pass on `rows`
+    rows sizes the reported pass to about `target_s` seconds."""
     import oracle
     import synth
     S, cp, H, G, d = w.total_tokens, w.cp, w.n_hq, w.n_kv, w.head_dim
@@ -57,6 +58,13 @@ def cpu_baseline_prefill(w, rows=64):
     t0 = time.perf_counter()
     oracle.partial_attention(qs, kb, vb, np.arange(rows), np.arange(n), None, w.softmax_scale, causal=False)
     dt = time.perf_counter() - t0
+    more = int(min(2048, max(rows, rows * target_s / max(dt, 1e-3))) // 64 * 64)
+    if more > rows:
+        rows = more
+        qs = synth.tensor_np(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, row_start=tail0, rows=rows)
+        t0 = time.perf_counter()
+        oracle.partial_attention(qs, kb, vb, np.arange(rows), np.arange(n), None, w.softmax_scale, causal=False)
+        dt = time.perf_counter() - t0
     flops = 4 * d * H * rows * n
     cores = len(os.sched_getaffinity(0))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
