@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (the cp ranks are emulated on it); "
@@ -226,6 +229,14 @@ def main():
     }
     del blocks, kshards, vshards
     torch.cuda.empty_cache()
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = src.numel() * 4
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the CPU")
         cb = cpu_baseline_prefill(wp)
