@@ -9,6 +9,7 @@
 namespace cpattn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -24,7 +25,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // Two fp32 -> packed bf16 pair, round to nearest even (gfx950 has a native
 // instruction for this conversion).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }

@@ -12,11 +12,13 @@
 // ragged end of a chunk.
 //
 // Kernels
-//   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 4 waves owns 32*4/HG
-//       query rows x HG query heads of one kv group; K and V tiles of 64 keys are
-//       staged in LDS and shared by the 4 waves. S^T = K Q^T and O^T = V^T P^T run
-//       on v_mfma_f32_32x32x16_bf16, so every lane owns one query column of both
-//       products and the softmax needs a single cross-lane exchange per tile.
+//   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 8 waves (two per
+//       SIMD) owns 32*8/HG query rows x HG query heads of one kv group; K and V
+//       tiles of 64 keys are staged in double-buffered LDS (the next tile's global
+//       loads are in flight while the current one computes) and shared by the 8
+//       waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
+//       every lane owns one query column of both products and the softmax needs a
+//       single cross-lane exchange per tile.
 //   ring_step_generic<T, D>  fp32 (and bf16 head_dim 512): one workgroup per
 //       (query row, query head), fp32 arithmetic throughout.
 #include "kernels.h"
@@ -65,10 +67,14 @@ __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, f
 // MFMA kernel (bf16)
 // ----------------------------------------------------------------------------
 
-constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
+constexpr int kBN = 64;            // keys per tile
+constexpr int kWaves = 8;          // two waves per SIMD: one runs MFMA while the other runs softmax
 constexpr int kThreads = 64 * kWaves;
 constexpr int kVStride = kBN + 8;  // padded row of the transposed V tile (bf16 elements)
+// Rescale threshold of the running max in the exp2 domain: the numerator and
+// denominator are only rescaled when the max grows by more than 2^8, so
+// exp2(s - m_ref) stays below 256.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
 __device__ __forceinline__ int k_swizzle(int row) {
@@ -77,22 +83,84 @@ __device__ __forceinline__ int k_swizzle(int row) {
   return (D == 64) ? ((row >> 1) & 7) : (row & 15);
 }
 
-// Slot of tile key kk inside its 16-key group of the transposed V tile: the
-// order in which the MFMA k-index runs through the keys of the P fragment.
-__device__ __forceinline__ int v_slot_of_group(int kg) {
-  // group of 4 consecutive keys 4kg..4kg+3 -> first slot
-  return (kg >> 2) * 16 + (kg & 1) * 8 + ((kg >> 1) & 1) * 4;
+// Slot of tile key `key` in a row of the transposed V tile: the order in which
+// the MFMA k index walks the keys of the P fragment (see the PV product).
+__device__ __forceinline__ int v_slot(int key) {
+  return (key >> 4) * 16 + ((key >> 2) & 1) * 8 + ((key >> 3) & 1) * 4 + (key & 3);
+}
+
+template <int D>
+struct TileRegs {
+  // this thread's share of one K tile and one V tile, in flight from HBM/L2
+  static constexpr int KCH = D / 8;                               // 16-byte chunks per row
+  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads; // K chunks per thread
+  u32x4_t k[KN];
+  u32x4_t v[2];
+};
+
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D> &r, const __bf16 *kbase, const __bf16 *vbase,
+                                          int64_t krow0, int k0, int kend, int64_t kv_stride, int g) {
+  constexpr int KCH = D / 8;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KN; ++i) {
+    const int x = tid + i * kThreads;
+    const int key = x / KCH;
+    const int ch = x - key * KCH;
+    r.k[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (x < kBN * KCH && k0 + key < kend)
+      r.k[i] = *reinterpret_cast<const u32x4_t *>(kbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
+  }
+  // V: one pair of keys x 8 elements per thread
+  const int kp = tid / KCH;
+  const int ch = tid - kp * KCH;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int key = 2 * kp + e;
+    r.v[e] = u32x4_t{0u, 0u, 0u, 0u};
+    if (kp < kBN / 2 && k0 + key < kend)
+      r.v[e] = *reinterpret_cast<const u32x4_t *>(vbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store(const TileRegs<D> &r, __bf16 *Ks, __bf16 *Vt) {
+  constexpr int KCH = D / 8;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KN; ++i) {
+    const int x = tid + i * kThreads;
+    const int key = x / KCH;
+    const int ch = x - key * KCH;
+    if (x < kBN * KCH)
+      *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.k[i];
+  }
+  const int kp = tid / KCH;
+  const int ch = tid - kp * KCH;
+  if (kp < kBN / 2) {
+    const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = ch * 8 + 2 * i;
+      const uint32_t lo = (r.v[0][i] & 0xFFFFu) | (r.v[1][i] << 16);
+      const uint32_t hi = (r.v[0][i] >> 16) | (r.v[1][i] & 0xFFFF0000u);
+      *reinterpret_cast<uint32_t *>(&Vt[d0 * kVStride + slot]) = lo;
+      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * kVStride + slot]) = hi;
+    }
+  }
 }
 
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, StepArgs a) {
+__global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArgs a) {
   constexpr int BM = 32 * kWaves / HG;          // query rows per workgroup
-  constexpr int KCH = D / 8;                    // 16-byte chunks per K row
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
+  constexpr int KSZ = kBN * D;                  // K tile (bf16 elements)
+  constexpr int VSZ = D * kVStride;             // transposed V tile
 
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[kBN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * kVStride];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -106,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
   const int si = find_seq(tab, unit);
   const int c = tab.c[si];
   const int nt = (c + BM - 1) / BM;
-  int lt = unit - tab.start[si];
+  const int lt = unit - tab.start[si];
   // tail-chunk tiles first (they see at least as many keys), each chunk in
   // descending row order
   const bool tail = lt < nt;
@@ -120,14 +188,21 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
   const int wrow0 = tile * BM + (wave / HG) * 32;           // wave's first row inside the chunk
   const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
 
-  // key segments that are not empty
+  // key segments that are not empty: (first row in the block, visible key count, diagonal?)
   int nseg = 0;
-  int seg_b[2];
   int64_t seg_row[2];
+  int seg_end[2];
+  bool seg_diag[2];
   {
-    const int bh = a.b_head, bt = a.b_tail;
-    if (bt <= qa) { seg_b[nseg] = bt; seg_row[nseg] = tab.row_off[si] + c; ++nseg; }
-    if (bh <= qa) { seg_b[nseg] = bh; seg_row[nseg] = tab.row_off[si]; ++nseg; }
+    const int bs[2] = {a.b_tail, a.b_head};
+    const int64_t rs[2] = {tab.row_off[si] + c, tab.row_off[si]};
+    for (int x = 0; x < 2; ++x) {
+      if (bs[x] > qa) continue;
+      seg_row[nseg] = rs[x];
+      seg_diag[nseg] = bs[x] == qa;
+      seg_end[nseg] = seg_diag[nseg] ? wg_row_end : c;
+      ++nseg;
+    }
   }
 
   const int row = wrow0 + qi;
@@ -151,6 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
     }
     return;
   }
+  const int n0 = (seg_end[0] + kBN - 1) / kBN;
+  const int ntiles = n0 + (nseg > 1 ? (seg_end[1] + kBN - 1) / kBN : 0);
 
   // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
@@ -169,7 +246,8 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
   }
 
   const float sl2 = a.scale * kLog2e;
-  float m_run = kNegInf;   // running max of raw scores q.k
+  const float thr = kRescaleLog2 / sl2;   // rescale threshold in raw-score units
+  float m_ref = kNegInf;   // reference max of raw scores q.k (numerator and denominator are relative to it)
   float l_run = 0.f;       // this lane's share of the denominator
   f32x16_t oacc[DB];
 #pragma unroll
@@ -180,66 +258,44 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
   const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k);
   const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v);
   const int64_t kv_stride = (int64_t)a.n_kv * D;   // elements between consecutive keys
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int sg = 0; sg < nseg; ++sg) {
-    const bool diag = seg_b[sg] == qa;
-    const int kend = diag ? wg_row_end : c;         // keys [0, kend) of the chunk can be visible
-    const int64_t krow0 = seg_row[sg];
-    for (int k0 = 0; k0 < kend; k0 += kBN) {
-      __syncthreads();   // previous tile fully consumed
-      // ---- stage K (swizzled rows) and V (transposed, MFMA k-order) into LDS
-#pragma unroll
-      for (int i = 0; i < (kBN * KCH) / kThreads; ++i) {
-        const int x = tid + i * kThreads;
-        const int key = x / KCH;
-        const int ch = x - key * KCH;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (k0 + key < kend)
-          val = *reinterpret_cast<const u32x4_t *>(kbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
-        *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = val;
-      }
-      for (int x = tid; x < (kBN / 4) * KCH; x += kThreads) {
-        const int kg = x / KCH;
-        const int ch = x - kg * KCH;
-        u32x4_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kg * 4 + e;
-          w[e] = u32x4_t{0u, 0u, 0u, 0u};
-          if (k0 + key < kend)
-            w[e] = *reinterpret_cast<const u32x4_t *>(vbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
-        }
-        const int slot = v_slot_of_group(kg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // d = ch*8 + 2i (low halves) and d = ch*8 + 2i + 1 (high halves)
-          const uint32_t lo01 = (w[0][i] & 0xFFFFu) | (w[1][i] << 16);
-          const uint32_t lo23 = (w[2][i] & 0xFFFFu) | (w[3][i] << 16);
-          const uint32_t hi01 = (w[0][i] >> 16) | (w[1][i] & 0xFFFF0000u);
-          const uint32_t hi23 = (w[2][i] >> 16) | (w[3][i] & 0xFFFF0000u);
-          const int d0 = ch * 8 + 2 * i;
-          typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-          *reinterpret_cast<u32x2_t *>(&Vt[d0 * kVStride + slot]) = u32x2_t{lo01, lo23};
-          *reinterpret_cast<u32x2_t *>(&Vt[(d0 + 1) * kVStride + slot]) = u32x2_t{hi01, hi23};
-        }
-      }
-      __syncthreads();
+  // tile 0 -> LDS buffer 0
+  TileRegs<D> nxt;
+  tile_load<D>(nxt, kbase, vbase, seg_row[0], 0, seg_end[0], kv_stride, g);
+  tile_store<D>(nxt, Ks[0], Vt[0]);
+  __syncthreads();
 
-      // this wave's rows [wrow0, wrow0+32): tile fully in the future of all of them?
-      if (diag && k0 > wrow0 + 31) continue;
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int sg = it < n0 ? 0 : 1;
+    const int k0 = (it < n0 ? it : it - n0) * kBN;
+    const int kend = seg_end[sg];
+    const bool diag = seg_diag[sg];
+    // prefetch tile it+1 into registers; it lands while this tile computes
+    if (it + 1 < ntiles) {
+      const int sn = (it + 1) < n0 ? 0 : 1;
+      const int kn = ((it + 1) < n0 ? it + 1 : it + 1 - n0) * kBN;
+      tile_load<D>(nxt, kbase, vbase, seg_row[sn], kn, seg_end[sn], kv_stride, g);
+    }
+
+    // a diagonal tile entirely in the future of this wave's rows contributes nothing
+    if (!(diag && k0 > wrow0 + 31)) {
       const bool need_mask = (k0 + kBN > kend) || (diag && k0 + kBN - 1 > wrow0);
+      const __bf16 *Kc = Ks[cur];
+      const __bf16 *Vc = Vt[cur];
 
       // ---- S^T = K Q^T : two 32-key blocks
       f32x16_t sacc[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[mb][r] = 0.f;
         const int key = mb * 32 + qi;
+        const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((hf ^ k_swizzle<D>(key)) * 8)]);
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 1; ks < KS; ++ks) {
           const int ch = ks * 2 + hf;
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
           sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
         }
       }
@@ -262,28 +318,32 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      if (m_new == kNegInf) continue;   // nothing visible for this query yet
-      const float alpha = exp2_fast((m_run - m_new) * sl2);
-      const float mref = m_new * sl2;
-      m_run = m_new;
+      if (__any(mx > m_ref + thr)) {
+        // the max grew past the threshold for some query of this wave: move every
+        // lane's reference to its current max (exact rescale)
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_ref = m_new;
+      }
+      const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
 
       uint32_t pk[2][8];
-      float psum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
           const float p1 = exp2_fast(fmaf(sacc[mb][r + 1], sl2, -mref));
-          psum += p0 + p1;
           pk[mb][r >> 1] = pack_bf16x2(p0, p1);
+          // denominator from the same rounded values the PV product uses
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][r >> 1]), ones, l_run,
+                                                  false);
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 
       // ---- O^T += V^T P^T : 4 k-steps of 16 keys
 #pragma unroll
@@ -295,17 +355,20 @@ __global__ __launch_bounds__(kThreads, 2) void ring_step_mfma(SeqTable tab, Step
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const bf16x8_t vf =
-              *reinterpret_cast<const bf16x8_t *>(&Vt[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
+              *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
         }
       }
     }
+
+    if (it + 1 < ntiles) tile_store<D>(nxt, Ks[cur ^ 1], Vt[cur ^ 1]);
+    __syncthreads();
   }
 
   // ---- epilogue: natural-log max, full denominator, optional merge, store
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
-  const float m_nat = (m_run == kNegInf) ? kNegInf : m_run * a.scale;
+  const float m_nat = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
   float w_old = 0.f, w_new = 1.f, m_out = m_nat;
   if (a.accumulate) {
     const float m_old = *mptr;
