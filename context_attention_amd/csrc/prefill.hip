@@ -98,30 +98,56 @@ struct TileRegs {
   u32x4_t v[2];
 };
 
+// Byte offsets (relative to the first key row of a tile) of this thread's K
+// and V loads; a thread without a share gets an offset past any tile, which
+// the buffer range check turns into zeros.
 template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D> &r, const __bf16 *kbase, const __bf16 *vbase,
-                                          int64_t krow0, int k0, int kend, int64_t kv_stride, int g) {
+struct TileOffsets {
+  uint32_t k[TileRegs<D>::KN];
+  uint32_t v[2];
+};
+
+constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
+constexpr int32_t kBufferWord3 = 0x00020000;   // raw buffer resource word 3 on gfx9
+
+template <int D>
+__device__ __forceinline__ TileOffsets<D> tile_offsets(uint32_t row_bytes, int g) {
   constexpr int KCH = D / 8;
+  TileOffsets<D> o;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::KN; ++i) {
     const int x = tid + i * kThreads;
     const int key = x / KCH;
     const int ch = x - key * KCH;
-    r.k[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (x < kBN * KCH && k0 + key < kend)
-      r.k[i] = *reinterpret_cast<const u32x4_t *>(kbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
+    o.k[i] = (x < kBN * KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
   }
-  // V: one pair of keys x 8 elements per thread
   const int kp = tid / KCH;
   const int ch = tid - kp * KCH;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int key = 2 * kp + e;
-    r.v[e] = u32x4_t{0u, 0u, 0u, 0u};
-    if (kp < kBN / 2 && k0 + key < kend)
-      r.v[e] = *reinterpret_cast<const u32x4_t *>(vbase + (krow0 + k0 + key) * kv_stride + g * D + ch * 8);
-  }
+  for (int e = 0; e < 2; ++e)
+    o.v[e] = (kp < kBN / 2) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+  return o;
+}
+
+// Loads the tile whose first key row starts at byte `tile_base` of the K / V
+// block; rows at or past `rows_left` read as zeros (buffer range check).
+template <int D>
+__device__ __forceinline__ void tile_load(TileRegs<D> &r, const TileOffsets<D> &o, const char *kblock,
+                                          const char *vblock, int64_t tile_base, int rows_left,
+                                          uint32_t row_bytes) {
+  const int64_t lim = (int64_t)rows_left * row_bytes;
+  const int32_t nrec = (int32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(kblock + tile_base), (short)0, nrec, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(vblock + tile_base), (short)0, nrec, kBufferWord3);
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::KN; ++i)
+    r.k[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k[i], 0, 0));
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    r.v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v[e], 0, 0));
 }
 
 template <int D>
@@ -188,22 +214,16 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
   const int wrow0 = tile * BM + (wave / HG) * 32;           // wave's first row inside the chunk
   const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
 
-  // key segments that are not empty: (first row in the block, visible key count, diagonal?)
-  int nseg = 0;
-  int64_t seg_row[2];
-  int seg_end[2];
-  bool seg_diag[2];
-  {
-    const int bs[2] = {a.b_tail, a.b_head};
-    const int64_t rs[2] = {tab.row_off[si] + c, tab.row_off[si]};
-    for (int x = 0; x < 2; ++x) {
-      if (bs[x] > qa) continue;
-      seg_row[nseg] = rs[x];
-      seg_diag[nseg] = bs[x] == qa;
-      seg_end[nseg] = seg_diag[nseg] ? wg_row_end : c;
-      ++nseg;
-    }
-  }
+  // key segments that are not empty, as (first row in the block, visible key
+  // count, diagonal?); the tail key chunk first
+  const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
+  const int nseg = (int)vis_t + (int)vis_h;
+  const int64_t s0_row = vis_t ? tab.row_off[si] + c : tab.row_off[si];
+  const bool s0_diag = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
+  const int s0_end = s0_diag ? wg_row_end : c;
+  const int64_t s1_row = tab.row_off[si];
+  const bool s1_diag = a.b_head == qa;
+  const int s1_end = s1_diag ? wg_row_end : c;
 
   const int row = wrow0 + qi;
   const bool row_ok = row < c;
@@ -226,8 +246,8 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
     }
     return;
   }
-  const int n0 = (seg_end[0] + kBN - 1) / kBN;
-  const int ntiles = n0 + (nseg > 1 ? (seg_end[1] + kBN - 1) / kBN : 0);
+  const int n0 = (s0_end + kBN - 1) / kBN;
+  const int ntiles = n0 + (nseg > 1 ? (s1_end + kBN - 1) / kBN : 0);
 
   // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
@@ -255,28 +275,30 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k);
-  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v);
-  const int64_t kv_stride = (int64_t)a.n_kv * D;   // elements between consecutive keys
+  const char *kblock = reinterpret_cast<const char *>(a.k);
+  const char *vblock = reinterpret_cast<const char *>(a.v);
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);   // bytes between consecutive keys
+  const TileOffsets<D> toff = tile_offsets<D>(row_bytes, g);
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // tile 0 -> LDS buffer 0
   TileRegs<D> nxt;
-  tile_load<D>(nxt, kbase, vbase, seg_row[0], 0, seg_end[0], kv_stride, g);
+  tile_load<D>(nxt, toff, kblock, vblock, s0_row * row_bytes, s0_end, row_bytes);
   tile_store<D>(nxt, Ks[0], Vt[0]);
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
-    const int sg = it < n0 ? 0 : 1;
-    const int k0 = (it < n0 ? it : it - n0) * kBN;
-    const int kend = seg_end[sg];
-    const bool diag = seg_diag[sg];
+    const bool first = it < n0;
+    const int k0 = (first ? it : it - n0) * kBN;
+    const int kend = first ? s0_end : s1_end;
+    const bool diag = first ? s0_diag : s1_diag;
     // prefetch tile it+1 into registers; it lands while this tile computes
     if (it + 1 < ntiles) {
-      const int sn = (it + 1) < n0 ? 0 : 1;
-      const int kn = ((it + 1) < n0 ? it + 1 : it + 1 - n0) * kBN;
-      tile_load<D>(nxt, kbase, vbase, seg_row[sn], kn, seg_end[sn], kv_stride, g);
+      const bool nfirst = (it + 1) < n0;
+      const int kn = (nfirst ? it + 1 : it + 1 - n0) * kBN;
+      const int64_t nrow = (nfirst ? s0_row : s1_row) + kn;
+      tile_load<D>(nxt, toff, kblock, vblock, nrow * row_bytes, (nfirst ? s0_end : s1_end) - kn, row_bytes);
     }
 
     // a diagonal tile entirely in the future of this wave's rows contributes nothing
