@@ -89,93 +89,134 @@ __device__ __forceinline__ int v_slot(int key) {
   return (key >> 4) * 16 + ((key >> 2) & 1) * 8 + ((key >> 3) & 1) * 4 + (key & 3);
 }
 
+// Per-thread byte offsets (relative to the first key row of a tile) of the K
+// and V staging loads; a thread without a share gets an offset past any tile,
+// which the buffer range check turns into zeros.
 template <int D>
-struct TileRegs {
-  // this thread's share of one K tile and one V tile, in flight from HBM/L2
-  static constexpr int KCH = D / 8;                               // 16-byte chunks per row
-  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads; // K chunks per thread
-  u32x4_t k[KN];
-  u32x4_t v[2];
-};
-
-// Byte offsets (relative to the first key row of a tile) of this thread's K
-// and V loads; a thread without a share gets an offset past any tile, which
-// the buffer range check turns into zeros.
-template <int D>
-struct TileOffsets {
-  uint32_t k[TileRegs<D>::KN];
+struct StageMap {
+  static constexpr int KCH = D / 8;                                 // 16-byte chunks per row
+  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads;  // K chunks per thread
+  uint32_t k[KN];
   uint32_t v[2];
 };
 
 constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
 constexpr int32_t kBufferWord3 = 0x00020000;   // raw buffer resource word 3 on gfx9
 
+// K: chunk x = tid + i*kThreads -> (key x / KCH, chunk x % KCH), consecutive lanes
+// read consecutive 16-byte chunks of a row. V: lane -> key pair tid % 32 and chunk
+// tid / 32, so the 64 lanes of a wave write 64 distinct banks of the transposed tile.
 template <int D>
-__device__ __forceinline__ TileOffsets<D> tile_offsets(uint32_t row_bytes, int g) {
+__device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   constexpr int KCH = D / 8;
-  TileOffsets<D> o;
+  StageMap<D> o;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KN; ++i) {
+  for (int i = 0; i < StageMap<D>::KN; ++i) {
     const int x = tid + i * kThreads;
     const int key = x / KCH;
     const int ch = x - key * KCH;
     o.k[i] = (x < kBN * KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
   }
-  const int kp = tid / KCH;
-  const int ch = tid - kp * KCH;
+  const int kp = tid & 31;
+  const int ch = tid >> 5;
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    o.v[e] = (kp < kBN / 2) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+    o.v[e] = (ch < KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
   return o;
 }
 
-// Loads the tile whose first key row starts at byte `tile_base` of the K / V
-// block; rows at or past `rows_left` read as zeros (buffer range check).
-template <int D>
-__device__ __forceinline__ void tile_load(TileRegs<D> &r, const TileOffsets<D> &o, const char *kblock,
-                                          const char *vblock, int64_t tile_base, int rows_left,
-                                          uint32_t row_bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *block, int64_t row, int rows_left,
+                                                           uint32_t row_bytes) {
   const int64_t lim = (int64_t)rows_left * row_bytes;
   const int32_t nrec = (int32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(kblock + tile_base), (short)0, nrec, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void *)(vblock + tile_base), (short)0, nrec, kBufferWord3);
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::KN; ++i)
-    r.k[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o.k[i], 0, 0));
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    r.v[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o.v[e], 0, 0));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(block + row * (int64_t)row_bytes), (short)0, nrec,
+                                           kBufferWord3);
 }
 
 template <int D>
-__device__ __forceinline__ void tile_store(const TileRegs<D> &r, __bf16 *Ks, __bf16 *Vt) {
+struct KRegs {
+  u32x4_t x[StageMap<D>::KN];
+};
+struct VRegs {
+  u32x4_t x[2];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k(KRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+  for (int i = 0; i < StageMap<D>::KN; ++i)
+    r.x[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.k[i], 0, 0));
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(VRegs &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    r.x[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.v[e], 0, 0));
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const KRegs<D> &r, __bf16 *Ks) {
   constexpr int KCH = D / 8;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < TileRegs<D>::KN; ++i) {
+  for (int i = 0; i < StageMap<D>::KN; ++i) {
     const int x = tid + i * kThreads;
     const int key = x / KCH;
     const int ch = x - key * KCH;
     if (x < kBN * KCH)
-      *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.k[i];
+      *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.x[i];
   }
-  const int kp = tid / KCH;
-  const int ch = tid - kp * KCH;
-  if (kp < kBN / 2) {
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(const VRegs &r, __bf16 *Vt) {
+  constexpr int KCH = D / 8;
+  const int tid = threadIdx.x;
+  const int kp = tid & 31;
+  const int ch = tid >> 5;
+  if (ch < KCH) {
     const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = ch * 8 + 2 * i;
-      const uint32_t lo = (r.v[0][i] & 0xFFFFu) | (r.v[1][i] << 16);
-      const uint32_t hi = (r.v[0][i] >> 16) | (r.v[1][i] & 0xFFFF0000u);
+      const uint32_t lo = (r.x[0][i] & 0xFFFFu) | (r.x[1][i] << 16);
+      const uint32_t hi = (r.x[0][i] >> 16) | (r.x[1][i] & 0xFFFF0000u);
       *reinterpret_cast<uint32_t *>(&Vt[d0 * kVStride + slot]) = lo;
       *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * kVStride + slot]) = hi;
     }
   }
 }
+
+// S^T = K Q^T for the 64 keys of a staged tile: two 32-key blocks.
+template <int D>
+__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[D / 16], f32x16_t (&sacc)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int qi = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int key = mb * 32 + qi;
+    const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((hf ^ k_swizzle<D>(key)) * 8)]);
+    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < D / 16; ++ks) {
+      const int ch = ks * 2 + hf;
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
+      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
+    }
+  }
+}
+
+// Tile geometry of flattened tile index t over the (up to two) key segments.
+struct Segs {
+  int n0;                 // tiles of segment 0
+  int64_t row[2];         // first key row of each segment in the block
+  int end[2];             // visible keys of each segment
+  bool diag[2];
+  __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
+  __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * kBN; }
+};
 
 template <int D, int HG>
 __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArgs a) {
@@ -214,16 +255,17 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
   const int wrow0 = tile * BM + (wave / HG) * 32;           // wave's first row inside the chunk
   const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
 
-  // key segments that are not empty, as (first row in the block, visible key
-  // count, diagonal?); the tail key chunk first
+  // key segments that are not empty, the tail key chunk first
   const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
   const int nseg = (int)vis_t + (int)vis_h;
-  const int64_t s0_row = vis_t ? tab.row_off[si] + c : tab.row_off[si];
-  const bool s0_diag = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
-  const int s0_end = s0_diag ? wg_row_end : c;
-  const int64_t s1_row = tab.row_off[si];
-  const bool s1_diag = a.b_head == qa;
-  const int s1_end = s1_diag ? wg_row_end : c;
+  Segs sg;
+  sg.row[0] = vis_t ? tab.row_off[si] + c : tab.row_off[si];
+  sg.diag[0] = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
+  sg.end[0] = sg.diag[0] ? wg_row_end : c;
+  sg.row[1] = tab.row_off[si];
+  sg.diag[1] = a.b_head == qa;
+  sg.end[1] = sg.diag[1] ? wg_row_end : c;
+  sg.n0 = (sg.end[0] + kBN - 1) / kBN;
 
   const int row = wrow0 + qi;
   const bool row_ok = row < c;
@@ -246,8 +288,7 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
     }
     return;
   }
-  const int n0 = (s0_end + kBN - 1) / kBN;
-  const int ntiles = n0 + (nseg > 1 ? (s1_end + kBN - 1) / kBN : 0);
+  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + kBN - 1) / kBN : 0);
 
   // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
@@ -278,112 +319,130 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
   const char *kblock = reinterpret_cast<const char *>(a.k);
   const char *vblock = reinterpret_cast<const char *>(a.v);
   const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);   // bytes between consecutive keys
-  const TileOffsets<D> toff = tile_offsets<D>(row_bytes, g);
+  const StageMap<D> smap = stage_map<D>(row_bytes, g);
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // tile 0 -> LDS buffer 0
-  TileRegs<D> nxt;
-  tile_load<D>(nxt, toff, kblock, vblock, s0_row * row_bytes, s0_end, row_bytes);
-  tile_store<D>(nxt, Ks[0], Vt[0]);
+  // Prologue: K and V of tile 0 and K of tile 1 into LDS. Through the loop the K
+  // pipeline runs one tile ahead of V: iteration `it` multiplies K of tile it+1
+  // (QK^T of the next tile, on the matrix cores) while the exponentials of tile
+  // it run on the vector ALUs, then V of tile it. A tile that lies entirely in
+  // the future of a wave's rows is masked to -inf and contributes zeros.
+  {
+    KRegs<D> kr;
+    VRegs vr;
+    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes));
+    load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
+    store_k<D>(kr, Ks[0]);
+    store_v<D>(vr, Vt[0]);
+    if (ntiles > 1) {
+      const int s1 = sg.seg(1), k1 = sg.k0(1);
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
+      store_k<D>(kr, Ks[1]);
+    }
+  }
   __syncthreads();
+
+  f32x16_t snext[2];
+  qk_tile<D>(Ks[0], qf, snext);
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
-    const bool first = it < n0;
-    const int k0 = (first ? it : it - n0) * kBN;
-    const int kend = first ? s0_end : s1_end;
-    const bool diag = first ? s0_diag : s1_diag;
-    // prefetch tile it+1 into registers; it lands while this tile computes
-    if (it + 1 < ntiles) {
-      const bool nfirst = (it + 1) < n0;
-      const int kn = (nfirst ? it + 1 : it + 1 - n0) * kBN;
-      const int64_t nrow = (nfirst ? s0_row : s1_row) + kn;
-      tile_load<D>(nxt, toff, kblock, vblock, nrow * row_bytes, (nfirst ? s0_end : s1_end) - kn, row_bytes);
+    const int sc = sg.seg(it);
+    const int k0 = sg.k0(it);
+    const int kend = sg.end[sc];
+    const bool diag = sg.diag[sc];
+
+    // global prefetch: K of tile it+2 and V of tile it+1
+    KRegs<D> kr;
+    VRegs vr;
+    const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
+    if (pk2) {
+      const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes));
+    }
+    if (pv1) {
+      const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
+      load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
     }
 
-    // a diagonal tile entirely in the future of this wave's rows contributes nothing
-    if (!(diag && k0 > wrow0 + 31)) {
-      const bool need_mask = (k0 + kBN > kend) || (diag && k0 + kBN - 1 > wrow0);
-      const __bf16 *Kc = Ks[cur];
-      const __bf16 *Vc = Vt[cur];
-
-      // ---- S^T = K Q^T : two 32-key blocks
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int key = mb * 32 + qi;
-        const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((hf ^ k_swizzle<D>(key)) * 8)]);
-        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0], f32x16_t{}, 0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < KS; ++ks) {
-          const int ch = ks * 2 + hf;
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
-          sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
-        }
-      }
-
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool vis = (kk < kend) && (!diag || kk <= row);
-            if (!vis) sacc[mb][r] = kNegInf;
-          }
-      }
-
-      // ---- online softmax (lane = query column; keys split over the two halves)
-      float mx = kNegInf;
+    f32x16_t sacc[2] = {snext[0], snext[1]};
+    if ((k0 + kBN > kend) || (diag && k0 + kBN - 1 > wrow0)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__any(mx > m_ref + thr)) {
-        // the max grew past the threshold for some query of this wave: move every
-        // lane's reference to its current max (exact rescale)
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_ref = m_new;
-      }
-      const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
-
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
-          const float p1 = exp2_fast(fmaf(sacc[mb][r + 1], sl2, -mref));
-          pk[mb][r >> 1] = pack_bf16x2(p0, p1);
-          // denominator from the same rounded values the PV product uses
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][r >> 1]), ones, l_run,
-                                                  false);
+        for (int r = 0; r < 16; ++r) {
+          const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = (kk < kend) && (!diag || kk <= row);
+          if (!vis) sacc[mb][r] = kNegInf;
         }
-
-      // ---- O^T += V^T P^T : 4 k-steps of 16 keys
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int mb = ks >> 1;
-        const int base = (ks & 1) * 4;
-        u32x4_t pw = {pk[mb][base], pk[mb][base + 1], pk[mb][base + 2], pk[mb][base + 3]};
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8_t vf =
-              *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
-        }
-      }
     }
 
-    if (it + 1 < ntiles) tile_store<D>(nxt, Ks[cur ^ 1], Vt[cur ^ 1]);
+    // ---- online softmax (lane = query column; keys split over the two halves)
+    float mx = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_ref + thr)) {
+      // the max grew past the threshold for some query of this wave: move every
+      // lane's reference to its current max (exact rescale)
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+
+    // ---- one scheduling region: QK^T of the next tile (matrix cores) interleaved
+    // with this tile's exponentials (vector ALUs), then this tile's PV product
+    qk_tile<D>(Ks[cur ^ 1], qf, snext);
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
+        const float p1 = exp2_fast(fmaf(sacc[mb][r + 1], sl2, -mref));
+        pk[mb][r >> 1] = pack_bf16x2(p0, p1);
+        // denominator from the same rounded values the PV product uses
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][r >> 1]), ones, l_run, false);
+      }
+    const __bf16 *Vc = Vt[cur];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int mb = ks >> 1;
+      const int base = (ks & 1) * 4;
+      u32x4_t pw = {pk[mb][base], pk[mb][base + 1], pk[mb][base + 2], pk[mb][base + 3]};
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+      }
+    }
+    // interleave: each QK^T MFMA with a share of the exponential work, then the
+    // PV MFMAs with the rest
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 16); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+
+    // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
+    if (pk2) store_k<D>(kr, Ks[cur]);
+    if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
     __syncthreads();
   }
 
