@@ -94,10 +94,11 @@ __device__ __forceinline__ int v_slot(int key) {
 // which the buffer range check turns into zeros.
 template <int D>
 struct StageMap {
-  static constexpr int KCH = D / 8;                                 // 16-byte chunks per row
-  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads;  // K chunks per thread
+  static constexpr int KCH = D / 8;                                     // 16-byte chunks per row
+  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads;      // K chunks per thread
+  static constexpr int VN = (kBN / 2 * KCH + kThreads - 1) / kThreads;  // V (key pair, chunk) per thread
   uint32_t k[KN];
-  uint32_t v[2];
+  uint32_t v[VN][2];
 };
 
 constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
@@ -105,7 +106,8 @@ constexpr int32_t kBufferWord3 = 0x00020000;   // raw buffer resource word 3 on 
 
 // K: chunk x = tid + i*kThreads -> (key x / KCH, chunk x % KCH), consecutive lanes
 // read consecutive 16-byte chunks of a row. V: lane -> key pair tid % 32 and chunk
-// tid / 32, so the 64 lanes of a wave write 64 distinct banks of the transposed tile.
+// tid / 32 (+ kThreads/32 per pass), so the 64 lanes of a wave write 64 distinct
+// banks of the transposed tile.
 template <int D>
 __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   constexpr int KCH = D / 8;
@@ -119,10 +121,13 @@ __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
     o.k[i] = (x < kBN * KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
   }
   const int kp = tid & 31;
-  const int ch = tid >> 5;
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    o.v[e] = (ch < KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+  for (int j = 0; j < StageMap<D>::VN; ++j) {
+    const int ch = (tid >> 5) + j * (kThreads / 32);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      o.v[j][e] = (ch < KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+  }
   return o;
 }
 
@@ -138,8 +143,9 @@ template <int D>
 struct KRegs {
   u32x4_t x[StageMap<D>::KN];
 };
+template <int D>
 struct VRegs {
-  u32x4_t x[2];
+  u32x4_t x[StageMap<D>::VN][2];
 };
 
 template <int D>
@@ -150,10 +156,12 @@ __device__ __forceinline__ void load_k(KRegs<D> &r, const StageMap<D> &o, __amdg
 }
 
 template <int D>
-__device__ __forceinline__ void load_v(VRegs &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
+__device__ __forceinline__ void load_v(VRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-  for (int e = 0; e < 2; ++e)
-    r.x[e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.v[e], 0, 0));
+  for (int j = 0; j < StageMap<D>::VN; ++j)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      r.x[j][e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.v[j][e], 0, 0));
 }
 
 template <int D>
@@ -171,20 +179,23 @@ __device__ __forceinline__ void store_k(const KRegs<D> &r, __bf16 *Ks) {
 }
 
 template <int D>
-__device__ __forceinline__ void store_v(const VRegs &r, __bf16 *Vt) {
+__device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
   constexpr int KCH = D / 8;
   const int tid = threadIdx.x;
   const int kp = tid & 31;
-  const int ch = tid >> 5;
-  if (ch < KCH) {
-    const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
+  const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = ch * 8 + 2 * i;
-      const uint32_t lo = (r.x[0][i] & 0xFFFFu) | (r.x[1][i] << 16);
-      const uint32_t hi = (r.x[0][i] >> 16) | (r.x[1][i] & 0xFFFF0000u);
-      *reinterpret_cast<uint32_t *>(&Vt[d0 * kVStride + slot]) = lo;
-      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * kVStride + slot]) = hi;
+  for (int j = 0; j < StageMap<D>::VN; ++j) {
+    const int ch = (tid >> 5) + j * (kThreads / 32);
+    if (ch < KCH) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = ch * 8 + 2 * i;
+        const uint32_t lo = (r.x[j][0][i] & 0xFFFFu) | (r.x[j][1][i] << 16);
+        const uint32_t hi = (r.x[j][0][i] >> 16) | (r.x[j][1][i] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t *>(&Vt[d0 * kVStride + slot]) = lo;
+        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * kVStride + slot]) = hi;
+      }
     }
   }
 }
@@ -219,7 +230,8 @@ struct Segs {
 };
 
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ring_step_mfma(SeqTable tab,
+                                                                                          StepArgs a) {
   constexpr int BM = 32 * kWaves / HG;          // query rows per workgroup
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
   // the future of a wave's rows is masked to -inf and contributes zeros.
   {
     KRegs<D> kr;
-    VRegs vr;
+    VRegs<D> vr;
     load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes));
     load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
     store_k<D>(kr, Ks[0]);
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
 
     // global prefetch: K of tile it+2 and V of tile it+1
     KRegs<D> kr;
-    VRegs vr;
+    VRegs<D> vr;
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
@@ -425,21 +437,6 @@ __global__ __launch_bounds__(kThreads) void ring_step_mfma(SeqTable tab, StepArg
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
     }
-    // interleave: each QK^T MFMA with a share of the exponential work, then the
-    // PV MFMAs with the rest
-#pragma unroll
-    for (int i = 0; i < 2 * (D / 16); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
     if (pk2) store_k<D>(kr, Ks[cur]);
     if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
