@@ -73,6 +73,22 @@ def cpu_baseline_prefill(w, rows=64, target_s=15.0):
             "seconds": dt}
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "context_attention_amd", "csrc", f), "rb").read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,14 +233,15 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "ring_step_mfma<128,4>",
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("ring_step"),
             "flops_per_launch": per_launch_flops, "avg_launch_ms": round(avg_launch_s * 1e3, 3),
         },
         "decode": {
             "value": round(dec_gbs, 1), "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
             "ms": round(float(np.mean(dec_ms)), 3), "bytes": dec_bytes,
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_partial")},
         },
     }
     del blocks, kshards, vshards
