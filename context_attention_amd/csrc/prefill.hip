@@ -67,10 +67,35 @@ __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, f
 // MFMA kernel (bf16)
 // ----------------------------------------------------------------------------
 
-constexpr int kBN = 64;            // keys per tile
-constexpr int kWaves = 8;          // two waves per SIMD: one runs MFMA while the other runs softmax
-constexpr int kThreads = 64 * kWaves;
-constexpr int kVStride = kBN + 8;  // padded row of the transposed V tile (bf16 elements)
+// Per head_dim configuration: keys per tile (BN), waves per workgroup (NW) and
+// whether K goes to LDS by buffer-to-LDS copies (no staging registers) or
+// through registers. head_dim 64/128: 8 waves, two per SIMD, so one wave's MFMAs
+// overlap the other's softmax. head_dim 512: the 32 x 512 fp32 accumulator of a
+// wave takes 256 registers, so one wave per SIMD with 512 registers, 32-key tiles
+// (two K and V buffers fit in 144 KB of LDS) and K copied straight into LDS.
+template <int D>
+struct Cfg;
+template <>
+struct Cfg<64> {
+  static constexpr int BN = 64, NW = 8, WPE = 2;
+  static constexpr bool DMA_K = false;
+};
+template <>
+struct Cfg<128> {
+  static constexpr int BN = 64, NW = 8, WPE = 2;
+  static constexpr bool DMA_K = false;
+};
+template <>
+struct Cfg<512> {
+  static constexpr int BN = 32, NW = 4, WPE = 1;
+  static constexpr bool DMA_K = true;
+};
+constexpr int kWideHalf = 256;   // head_dim 512: each wave of a pair owns half of d
+template <int D>
+constexpr int kThreadsOf = 64 * Cfg<D>::NW;
+template <int D>
+constexpr int kVStrideOf = Cfg<D>::BN + 8;   // padded row of the transposed V tile (bf16 elements)
+
 // Rescale threshold of the running max in the exp2 domain: the numerator and
 // denominator are only rescaled when the max grows by more than 2^8, so
 // exp2(s - m_ref) stays below 256.
@@ -92,41 +117,59 @@ __device__ __forceinline__ int v_slot(int key) {
 // Per-thread byte offsets (relative to the first key row of a tile) of the K
 // and V staging loads; a thread without a share gets an offset past any tile,
 // which the buffer range check turns into zeros.
+//   K through registers: chunk x = tid + i*threads -> (key x / KCH, chunk x % KCH),
+//     consecutive lanes read consecutive 16-byte chunks of a row.
+//   K straight into LDS: lane L of a wave writes bytes [16L, 16L+16) of the 1 KB
+//     chunk the wave names, so lane L loads the global chunk that belongs at that
+//     position of the swizzled tile.
+//   V (transposed on the way into LDS, so through registers): lane -> key pair
+//     tid % (BN/2) and chunk tid / (BN/2) (+ threads/(BN/2) per pass), so lanes
+//     of a wave write distinct banks of the transposed tile.
 template <int D>
 struct StageMap {
-  static constexpr int KCH = D / 8;                                     // 16-byte chunks per row
-  static constexpr int KN = (kBN * KCH + kThreads - 1) / kThreads;      // K chunks per thread
-  static constexpr int VN = (kBN / 2 * KCH + kThreads - 1) / kThreads;  // V (key pair, chunk) per thread
+  static constexpr int BN = Cfg<D>::BN, T = kThreadsOf<D>, KCH = D / 8, P2 = BN / 2;
+  static constexpr int KN = Cfg<D>::DMA_K ? (BN * D * 2 / 1024) / Cfg<D>::NW : (BN * KCH + T - 1) / T;
+  static constexpr int VN = (P2 * KCH + T - 1) / T;
   uint32_t k[KN];
   uint32_t v[VN][2];
 };
 
 constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
 constexpr int32_t kBufferWord3 = 0x00020000;   // raw buffer resource word 3 on gfx9
+constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0), other counters unconstrained
 
-// K: chunk x = tid + i*kThreads -> (key x / KCH, chunk x % KCH), consecutive lanes
-// read consecutive 16-byte chunks of a row. V: lane -> key pair tid % 32 and chunk
-// tid / 32 (+ kThreads/32 per pass), so the 64 lanes of a wave write 64 distinct
-// banks of the transposed tile.
 template <int D>
 __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
-  constexpr int KCH = D / 8;
+  using M = StageMap<D>;
   StageMap<D> o;
   const int tid = threadIdx.x;
+  if constexpr (Cfg<D>::DMA_K) {
+    constexpr int ROWS_PER_KB = 1024 / (D * 2);
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int i = 0; i < StageMap<D>::KN; ++i) {
-    const int x = tid + i * kThreads;
-    const int key = x / KCH;
-    const int ch = x - key * KCH;
-    o.k[i] = (x < kBN * KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+    for (int i = 0; i < M::KN; ++i) {
+      const int q = wave * M::KN + i;                    // 1 KB chunk of the tile
+      const int key = q * ROWS_PER_KB + lane / M::KCH;
+      const int pc = lane % M::KCH;                      // physical chunk in the LDS row
+      const int ch = pc ^ k_swizzle<D>(key);             // logical chunk it holds
+      o.k[i] = key * row_bytes + (uint32_t)(g * D * 2 + ch * 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < M::KN; ++i) {
+      const int x = tid + i * M::T;
+      const int key = x / M::KCH;
+      const int ch = x - key * M::KCH;
+      o.k[i] = (x < M::BN * M::KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+    }
   }
-  const int kp = tid & 31;
+  const int kp = tid % M::P2;
 #pragma unroll
-  for (int j = 0; j < StageMap<D>::VN; ++j) {
-    const int ch = (tid >> 5) + j * (kThreads / 32);
+  for (int j = 0; j < M::VN; ++j) {
+    const int ch = tid / M::P2 + j * (M::T / M::P2);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      o.v[j][e] = (ch < KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+      o.v[j][e] = (ch < M::KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
   }
   return o;
 }
@@ -141,18 +184,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *block, i
 
 template <int D>
 struct KRegs {
-  u32x4_t x[StageMap<D>::KN];
+  u32x4_t x[Cfg<D>::DMA_K ? 1 : StageMap<D>::KN];
 };
 template <int D>
 struct VRegs {
   u32x4_t x[StageMap<D>::VN][2];
 };
 
+// Starts the copy of K tile into its LDS buffer: through registers (load_k, then
+// store_k) or straight into LDS (complete once vmcnt reaches zero).
 template <int D>
-__device__ __forceinline__ void load_k(KRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
+__device__ __forceinline__ void load_k(KRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs, __bf16 *Ks) {
+  if constexpr (Cfg<D>::DMA_K) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < StageMap<D>::KN; ++i)
-    r.x[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.k[i], 0, 0));
+    for (int i = 0; i < StageMap<D>::KN; ++i) {
+      __bf16 *dst = Ks + (wave * StageMap<D>::KN + i) * 512;   // 1 KB chunk
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16, o.k[i], 0,
+                                               0, 0);
+    }
+#endif
+  } else {
+#pragma unroll
+    for (int i = 0; i < StageMap<D>::KN; ++i)
+      r.x[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.k[i], 0, 0));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const KRegs<D> &r, __bf16 *Ks) {
+  if constexpr (!Cfg<D>::DMA_K) {
+    using M = StageMap<D>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < M::KN; ++i) {
+      const int x = tid + i * M::T;
+      const int key = x / M::KCH;
+      const int ch = x - key * M::KCH;
+      if (x < M::BN * M::KCH)
+        *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.x[i];
+    }
+  }
 }
 
 template <int D>
@@ -165,48 +238,36 @@ __device__ __forceinline__ void load_v(VRegs<D> &r, const StageMap<D> &o, __amdg
 }
 
 template <int D>
-__device__ __forceinline__ void store_k(const KRegs<D> &r, __bf16 *Ks) {
-  constexpr int KCH = D / 8;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < StageMap<D>::KN; ++i) {
-    const int x = tid + i * kThreads;
-    const int key = x / KCH;
-    const int ch = x - key * KCH;
-    if (x < kBN * KCH)
-      *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.x[i];
-  }
-}
-
-template <int D>
 __device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
-  constexpr int KCH = D / 8;
+  using M = StageMap<D>;
+  constexpr int VS = kVStrideOf<D>;
   const int tid = threadIdx.x;
-  const int kp = tid & 31;
+  const int kp = tid % M::P2;
   const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
 #pragma unroll
-  for (int j = 0; j < StageMap<D>::VN; ++j) {
-    const int ch = (tid >> 5) + j * (kThreads / 32);
-    if (ch < KCH) {
+  for (int j = 0; j < M::VN; ++j) {
+    const int ch = tid / M::P2 + j * (M::T / M::P2);
+    if (ch < M::KCH) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = ch * 8 + 2 * i;
         const uint32_t lo = (r.x[j][0][i] & 0xFFFFu) | (r.x[j][1][i] << 16);
         const uint32_t hi = (r.x[j][0][i] >> 16) | (r.x[j][1][i] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t *>(&Vt[d0 * kVStride + slot]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * kVStride + slot]) = hi;
+        *reinterpret_cast<uint32_t *>(&Vt[d0 * VS + slot]) = lo;
+        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VS + slot]) = hi;
       }
     }
   }
 }
 
-// S^T = K Q^T for the 64 keys of a staged tile: two 32-key blocks.
+// S^T = K Q^T for the keys of a staged tile, in 32-key blocks.
 template <int D>
-__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[D / 16], f32x16_t (&sacc)[2]) {
+__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[D / 16],
+                                        f32x16_t (&sacc)[Cfg<D>::BN / 32]) {
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, hf = lane >> 5;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < Cfg<D>::BN / 32; ++mb) {
     const int key = mb * 32 + qi;
     const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((hf ^ k_swizzle<D>(key)) * 8)]);
     sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0], f32x16_t{}, 0, 0, 0);
@@ -220,23 +281,29 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[D
 }
 
 // Tile geometry of flattened tile index t over the (up to two) key segments.
+template <int BN>
 struct Segs {
   int n0;                 // tiles of segment 0
   int64_t row[2];         // first key row of each segment in the block
   int end[2];             // visible keys of each segment
   bool diag[2];
   __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
-  __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * kBN; }
+  __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * BN; }
 };
 
 template <int D, int HG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void ring_step_mfma(SeqTable tab,
-                                                                                          StepArgs a) {
-  constexpr int BM = 32 * kWaves / HG;          // query rows per workgroup
+__global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
+void ring_step_mfma(SeqTable tab, StepArgs a) {
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int NW = Cfg<D>::NW;
+  constexpr int MB = BN / 32;                   // 32-key blocks per tile
+  constexpr int PKS = BN / 16;                  // 16-key MFMA k-steps of the PV product
+  constexpr int BM = 32 * NW / HG;              // query rows per workgroup
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
-  constexpr int KSZ = kBN * D;                  // K tile (bf16 elements)
-  constexpr int VSZ = D * kVStride;             // transposed V tile
+  constexpr int VS = kVStrideOf<D>;
+  constexpr int KSZ = BN * D;                   // K tile (bf16 elements)
+  constexpr int VSZ = D * VS;                   // transposed V tile
 
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
@@ -270,14 +337,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // key segments that are not empty, the tail key chunk first
   const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
   const int nseg = (int)vis_t + (int)vis_h;
-  Segs sg;
+  Segs<BN> sg;
   sg.row[0] = vis_t ? tab.row_off[si] + c : tab.row_off[si];
   sg.diag[0] = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
   sg.end[0] = sg.diag[0] ? wg_row_end : c;
   sg.row[1] = tab.row_off[si];
   sg.diag[1] = a.b_head == qa;
   sg.end[1] = sg.diag[1] ? wg_row_end : c;
-  sg.n0 = (sg.end[0] + kBN - 1) / kBN;
+  sg.n0 = (sg.end[0] + BN - 1) / BN;
 
   const int row = wrow0 + qi;
   const bool row_ok = row < c;
@@ -300,7 +367,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     return;
   }
-  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + kBN - 1) / kBN : 0);
+  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + BN - 1) / BN : 0);
 
   // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
@@ -342,19 +409,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   {
     KRegs<D> kr;
     VRegs<D> vr;
-    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes));
+    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
     load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
     store_k<D>(kr, Ks[0]);
     store_v<D>(vr, Vt[0]);
     if (ntiles > 1) {
       const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
       store_k<D>(kr, Ks[1]);
     }
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
-  f32x16_t snext[2];
+  f32x16_t snext[MB];
   qk_tile<D>(Ks[0], qf, snext);
 
   for (int it = 0; it < ntiles; ++it) {
@@ -364,23 +432,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    // global prefetch: K of tile it+2 and V of tile it+1
+    // prefetch: K of tile it+2 (into the LDS buffer of K of tile it, read in the
+    // previous iteration, or into registers) and V of tile it+1 into registers
     KRegs<D> kr;
     VRegs<D> vr;
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes));
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
     }
     if (pv1) {
       const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
       load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
     }
 
-    f32x16_t sacc[2] = {snext[0], snext[1]};
-    if ((k0 + kBN > kend) || (diag && k0 + kBN - 1 > wrow0)) {
+    f32x16_t sacc[MB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb) sacc[mb] = snext[mb];
+    if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -392,7 +463,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // ---- online softmax (lane = query column; keys split over the two halves)
     float mx = kNegInf;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -410,12 +481,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
 
-    // ---- one scheduling region: QK^T of the next tile (matrix cores) interleaved
-    // with this tile's exponentials (vector ALUs), then this tile's PV product
+    // ---- one scheduling region: QK^T of the next tile (matrix cores) with this
+    // tile's exponentials (vector ALUs), then this tile's PV product
     qk_tile<D>(Ks[cur ^ 1], qf, snext);
-    uint32_t pk[2][8];
+    uint32_t pk[MB][8];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
@@ -426,20 +497,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     const __bf16 *Vc = Vt[cur];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < PKS; ++ks) {
       const int mb = ks >> 1;
       const int base = (ks & 1) * 4;
       u32x4_t pw = {pk[mb][base], pk[mb][base + 1], pk[mb][base + 2], pk[mb][base + 3]};
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * kVStride + ks * 16 + 8 * hf]);
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * VS + ks * 16 + 8 * hf]);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
     }
+
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
     if (pk2) store_k<D>(kr, Ks[cur]);
     if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
+    if constexpr (Cfg<D>::DMA_K) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
@@ -459,6 +532,255 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 #pragma unroll
   for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
+      f32x4_t o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+      if (a.accumulate) {
+        const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
+        o = old * w_old + o * w_new;
+      }
+      *reinterpret_cast<f32x4_t *>(p) = o;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// head_dim 512 (bf16): wave pairs split d.
+// ----------------------------------------------------------------------------
+// A workgroup of 4 waves (one per SIMD) is two pairs; the two waves of a pair own
+// the same 32 query rows and one half of d each: Q and the output accumulator of
+// a wave cover its 256 columns (64 + 128 registers). QK^T is split over d too:
+// each wave multiplies its half, the pair exchanges the two partial 32 x 32 score
+// tiles through LDS and both add them, so both hold the full scores and run the
+// same softmax; the PV product then fills each wave's half of the output. Keys
+// come in 32-key tiles; K is copied straight into LDS, V is transposed through
+// registers.
+template <int HG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ring_step_wide(SeqTable tab, StepArgs a) {
+  constexpr int D = 512;
+  constexpr int BN = Cfg<D>::BN;                // 32 keys per tile
+  constexpr int NP = Cfg<D>::NW / 2;            // pairs per workgroup
+  constexpr int BM = 32 * NP / HG;              // query rows per workgroup
+  constexpr int KSH = kWideHalf / 16;           // QK^T k-steps over one half of d
+  constexpr int DBH = kWideHalf / 32;           // output d blocks of one half
+  constexpr int VS = kVStrideOf<D>;
+  constexpr int KSZ = BN * D;
+  constexpr int VSZ = D * VS;
+
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
+  __shared__ __attribute__((aligned(16))) f32x16_t Sx[Cfg<D>::NW][64];   // partial scores, one tile per wave
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int qi = lane & 31;
+  const int hf = lane >> 5;
+  const int pair = wave >> 1, dh = wave & 1;
+
+  const int n_hg = a.n_hq / HG;
+  const int unit = blockIdx.x / n_hg;
+  const int hg = blockIdx.x - unit * n_hg;
+  const int si = find_seq(tab, unit);
+  const int c = tab.c[si];
+  const int nt = (c + BM - 1) / BM;
+  const int lt = unit - tab.start[si];
+  const bool tail = lt < nt;
+  const int tile = tail ? (nt - 1 - lt) : (nt - 1 - (lt - nt));
+  const int qa = tail ? a.a_tail : a.a_head;
+  const int64_t qrow0 = tab.row_off[si] + (tail ? c : 0);
+
+  const int h = hg * HG + (pair % HG);
+  const int rep = a.n_hq / a.n_kv;
+  const int g = h / rep;
+  const int wrow0 = tile * BM + (pair / HG) * 32;
+  const int wg_row_end = min(c, tile * BM + BM);
+
+  const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
+  const int nseg = (int)vis_t + (int)vis_h;
+  Segs<BN> sg;
+  sg.row[0] = vis_t ? tab.row_off[si] + c : tab.row_off[si];
+  sg.diag[0] = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
+  sg.end[0] = sg.diag[0] ? wg_row_end : c;
+  sg.row[1] = tab.row_off[si];
+  sg.diag[1] = a.b_head == qa;
+  sg.end[1] = sg.diag[1] ? wg_row_end : c;
+  sg.n0 = (sg.end[0] + BN - 1) / BN;
+
+  const int row = wrow0 + qi;
+  const bool row_ok = row < c;
+  const int64_t grow = qrow0 + row;
+  float *mptr = a.m + (grow * a.n_hq + h);
+  float *dptr = a.den + (grow * a.n_hq + h);
+  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D + dh * kWideHalf;
+
+  if (nseg == 0) {
+    if (!a.accumulate && row_ok) {
+      if (hf == 0 && dh == 0) store_stats(mptr, dptr, kNegInf, 0.f);
+#pragma unroll
+      for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + BN - 1) / BN : 0);
+
+  // Q fragments of this wave's half of d
+  bf16x8_t qf[KSH];
+  {
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + (grow * a.n_hq + h) * (int64_t)D + dh * kWideHalf + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks)
+      qf[ks] = row_ok ? *reinterpret_cast<const bf16x8_t *>(qp + ks * 16)
+                      : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  const float thr = kRescaleLog2 / sl2;
+  float m_ref = kNegInf;
+  float l_run = 0.f;
+  f32x16_t oacc[DBH];
+#pragma unroll
+  for (int db = 0; db < DBH; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  const char *kblock = reinterpret_cast<const char *>(a.k);
+  const char *vblock = reinterpret_cast<const char *>(a.v);
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
+  const StageMap<D> smap = stage_map<D>(row_bytes, g);
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // partial S^T = K Q^T over this wave's half of d for the 32 keys of a tile
+  auto qk_half = [&](const __bf16 *Kc, f32x16_t &sp) {
+    const int key = qi;
+    sp = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) {
+      const int ch = (dh * KSH + ks) * 2 + hf;
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
+      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sp, 0, 0, 0);
+    }
+  };
+
+  {
+    KRegs<D> kr;
+    VRegs<D> vr;
+    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
+    load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
+    store_v<D>(vr, Vt[0]);
+    if (ntiles > 1) {
+      const int s1 = sg.seg(1), k1 = sg.k0(1);
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  f32x16_t spart;
+  qk_half(Ks[0], spart);
+  Sx[wave][lane] = spart;
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int sc = sg.seg(it);
+    const int k0 = sg.k0(it);
+    const int kend = sg.end[sc];
+    const bool diag = sg.diag[sc];
+
+    KRegs<D> kr;
+    VRegs<D> vr;
+    const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
+    if (pk2) {
+      const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
+      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
+    }
+    if (pv1) {
+      const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
+      load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
+    }
+
+    // full scores of tile it = own partial + the partner's partial
+    f32x16_t sacc = spart + Sx[wave ^ 1][lane];
+    __syncthreads();   // both partials read before either is overwritten
+
+    if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const bool vis = (kk < kend) && (!diag || kk <= row);
+        if (!vis) sacc[r] = kNegInf;
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_ref + thr)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+
+    qk_half(Ks[cur ^ 1], spart);   // next tile's partial scores
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(fmaf(sacc[r], sl2, -mref));
+      const float p1 = exp2_fast(fmaf(sacc[r + 1], sl2, -mref));
+      pk[r >> 1] = pack_bf16x2(p0, p1);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), ones, l_run, false);
+    }
+    const __bf16 *Vc = Vt[cur];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int base = ks * 4;
+      u32x4_t pw = {pk[base], pk[base + 1], pk[base + 2], pk[base + 3]};
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int db = 0; db < DBH; ++db) {
+        const int d0 = dh * kWideHalf + db * 32;
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(d0 + qi) * VS + ks * 16 + 8 * hf]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+      }
+    }
+
+    Sx[wave][lane] = spart;
+    if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // both waves of a pair read the old max and denominator; every wave reaches the
+  // barrier before one of them overwrites them
+  float m_old = kNegInf, d_old = 0.f;
+  if (a.accumulate && row_ok) {
+    m_old = *mptr;
+    d_old = *dptr;
+  }
+  __syncthreads();
+  if (!row_ok) return;
+  const float m_nat = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
+  float w_old = 0.f, w_new = 1.f, m_out = m_nat;
+  if (a.accumulate) {
+    merge_weights(m_old, m_nat, m_out, w_old, w_new);
+    const float d_out = w_old * d_old + w_new * l_tot;
+    if (hf == 0 && dh == 0) store_stats(mptr, dptr, m_out, d_out);
+  } else if (hf == 0 && dh == 0) {
+    store_stats(mptr, dptr, m_nat, l_tot);
+  }
+#pragma unroll
+  for (int db = 0; db < DBH; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
@@ -604,16 +926,35 @@ template <int D, int HG>
 hipError_t launch_mfma(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
   const int n_hg = a.n_hq / HG;
   const int64_t blocks = (int64_t)units * n_hg;
-  hipLaunchKernelGGL((ring_step_mfma<D, HG>), dim3((unsigned)blocks), dim3(kThreads), 0, s, t, a);
+  hipLaunchKernelGGL((ring_step_mfma<D, HG>), dim3((unsigned)blocks), dim3(kThreadsOf<D>), 0, s, t, a);
   return hipGetLastError();
+}
+
+template <int HG>
+hipError_t launch_wide(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
+  const int n_hg = a.n_hq / HG;
+  const int64_t blocks = (int64_t)units * n_hg;
+  hipLaunchKernelGGL((ring_step_wide<HG>), dim3((unsigned)blocks), dim3(256), 0, s, t, a);
+  return hipGetLastError();
+}
+
+// heads per workgroup: up to 4 query heads of one kv group (2 for head_dim 512,
+// whose workgroup holds two wave pairs)
+int pick_hg_d(int d, int rep) {
+  const int hg = pick_hg(rep);
+  return (d == 512 && hg > 2) ? 2 : hg;
 }
 
 template <int D>
 hipError_t launch_mfma_d(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
-  const int hg = pick_hg(a.n_hq / a.n_kv);
-  if (hg == 4) return launch_mfma<D, 4>(t, a, units, s);
-  if (hg == 2) return launch_mfma<D, 2>(t, a, units, s);
-  return launch_mfma<D, 1>(t, a, units, s);
+  if constexpr (D == 512) {
+    return pick_hg_d(512, a.n_hq / a.n_kv) == 2 ? launch_wide<2>(t, a, units, s) : launch_wide<1>(t, a, units, s);
+  } else {
+    const int hg = pick_hg(a.n_hq / a.n_kv);
+    if (hg == 4) return launch_mfma<D, 4>(t, a, units, s);
+    if (hg == 2) return launch_mfma<D, 2>(t, a, units, s);
+    return launch_mfma<D, 1>(t, a, units, s);
+  }
 }
 
 template <typename T, int D>
@@ -623,18 +964,20 @@ hipError_t launch_generic(const SeqTable &t, const StepArgs &a, int units, hipSt
   return hipGetLastError();
 }
 
-// The MFMA kernel covers bf16 with head_dim 64 and 128.
-bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || d == 128); }
+// The MFMA kernel covers bf16 (head_dim 64, 128, 512); fp32 runs the generic kernel.
+bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || d == 128 || d == 512); }
 
 int rows_per_unit(int dtype, int d, int rep) {
-  return use_mfma(dtype, d) ? 32 * kWaves / pick_hg(rep) : 1;
+  if (!use_mfma(dtype, d)) return 1;
+  if (d == 512) return 32 * (Cfg<512>::NW / 2) / pick_hg_d(512, rep);
+  return 32 * Cfg<128>::NW / pick_hg(rep);
 }
 
 hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
   if (dtype == CPATTN_DT_BF16) {
     if (d == 64) return launch_mfma_d<64>(t, a, units, s);
     if (d == 128) return launch_mfma_d<128>(t, a, units, s);
-    return launch_generic<__bf16, 512>(t, a, units, s);
+    return launch_mfma_d<512>(t, a, units, s);
   }
   if (d == 64) return launch_generic<float, 64>(t, a, units, s);
   if (d == 128) return launch_generic<float, 128>(t, a, units, s);
@@ -705,7 +1048,7 @@ extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t
     while (i < desc->num_seqs && t.n < kMaxSeq) {
       const int64_t c = (cu[i + 1] - cu[i]) / (2 * cp);
       const int64_t u = mfma ? 2 * ((c + rpu - 1) / rpu) : 2 * c;
-      const int64_t blocks_after = (units + u) * (mfma ? desc->n_hq / pick_hg(rep) : 1);
+      const int64_t blocks_after = (units + u) * (mfma ? desc->n_hq / pick_hg_d(d, rep) : 1);
       if (t.n > 0 && blocks_after > 0x7FFFFFFFLL) break;
       if (blocks_after > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
       t.c[t.n] = (int32_t)c;

@@ -24,6 +24,8 @@ CASES = [
     ("mha-bf16-d64-varlen", [2 * 2 * 70, 2 * 2 * 130, 2 * 2 * 9], 2, 4, 4, 64, "bf16", 0.5),
     ("gqa2-bf16-d128-cp3", [2 * 3 * 100, 2 * 3 * 33], 3, 4, 2, 128, "bf16", 0.5),
     ("mha-bf16-d512-varlen", [2 * 2 * 37, 2 * 2 * 20], 2, 2, 2, 512, "bf16", 0.5),
+    ("gqa2-bf16-d512-cp4", [2 * 4 * 70, 2 * 4 * 33], 4, 4, 2, 512, "bf16", 0.5),
+    ("mha-bf16-d512-cp3-long-chunks", [2 * 3 * 150], 3, 2, 2, 512, "bf16", 0.5),
     ("gqa2-f32-d128", [2 * 2 * 50], 2, 4, 2, 128, "f32", 1.0),
     ("gqa2-f32-d512", [2 * 2 * 12], 2, 2, 1, 512, "f32", 1.0),
     ("cp1-bf16-d128", [300, 64], 1, 8, 2, 128, "bf16", 0.5),
@@ -228,3 +230,41 @@ def test_long_context_rank0_share_sampled():
     go = out[torch.from_numpy(sample).cuda()][:, heads].cpu().numpy()
     gl = lse[torch.from_numpy(sample).cuda()][:, heads].cpu().numpy()
     compare("long rank 0 sampled", go, gl, wo, wl, TOL_BF16)
+
+
+def test_wide_head_varlen_workload_sampled():
+    """The wide-head varlen workload (6 packed sequences of 9376..16048 tokens,
+    cp = 4, 64 heads, head_dim 512, bf16): every rank's full ring, fused, then
+    sampled rows of ranks 0 and 3 against the oracle on heads 5 and 42."""
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    w = synth.WORKLOADS["varlen"]
+    T, cp, d, H = w.total_tokens, w.cp, w.head_dim, w.n_hq
+    log(f"[prefill full] {w.name}")
+    cu = w.cu_seqlens
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (T, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (T, w.n_kv, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (T, w.n_kv, d), w.scale_in, w.dtype, "cuda")
+    local = local_buffers(ca, cu, cp, [q, k, v])
+    del q, k, v
+    desc = ca.PrefillDesc(cp=cp, cu_seqlens=cu, n_hq=H, n_kv=w.n_kv, head_dim=d, dtype=w.dtype,
+                          scale=w.softmax_scale)
+    res = run_ring(ca, desc, local, fused=True)
+    heads = [5, 42]
+    rng = np.random.default_rng(5)
+    for r in (0, 3):
+        pos = local[r][0]
+        rows = np.unique(np.concatenate([[0, len(pos) - 1], rng.integers(0, len(pos), 10)]))
+        for h in heads:
+            kh = synth.head_slice_np(w.seed, synth.TENSOR_K, (T, w.n_kv, d), h, w.scale_in, w.dtype)
+            vh = synth.head_slice_np(w.seed, synth.TENSOR_V, (T, w.n_kv, d), h, w.scale_in, w.dtype)
+            for row in rows:
+                g = int(pos[row])
+                si = int(np.searchsorted(cu, g, side="right") - 1)
+                a0, a1 = int(cu[si]), int(cu[si + 1])
+                qh = synth.values_at_np(w.seed, synth.TENSOR_Q, (g * H + h) * d + np.arange(d), w.scale_in, w.dtype)
+                wo, wl = oracle.attention_reference_rows(qh[None, None, :], np.array([g - a0]), kh[a0:a1], vh[a0:a1],
+                                                         w.softmax_scale)
+                compare(f"varlen r{r} row {row} head {h}", res[r]["out"][row, h].cpu().numpy()[None, None],
+                        res[r]["lse"][row, h].cpu().numpy()[None, None], wo, wl, TOL_BF16)
