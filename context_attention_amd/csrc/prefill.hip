@@ -67,27 +67,27 @@ __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, f
 // MFMA kernel (bf16)
 // ----------------------------------------------------------------------------
 
-// Per head_dim configuration: keys per tile (BN), waves per workgroup (NW) and
-// whether K goes to LDS by buffer-to-LDS copies (no staging registers) or
-// through registers. head_dim 64/128: 8 waves, two per SIMD, so one wave's MFMAs
-// overlap the other's softmax. head_dim 512: the 32 x 512 fp32 accumulator of a
-// wave takes 256 registers, so one wave per SIMD with 512 registers, 32-key tiles
-// (two K and V buffers fit in 144 KB of LDS) and K copied straight into LDS.
+// Per head_dim configuration: keys per tile (BN), waves per workgroup (NW),
+// 32-row blocks per wave (NB) and whether K goes to LDS by buffer-to-LDS copies
+// (no staging registers) or through registers. head_dim 64/128: 8 waves, two
+// per SIMD, so one wave's MFMAs overlap the other's softmax and latencies
+// (a wave per SIMD with two row blocks halves LDS reads per MFMA but measured
+// half the speed). head_dim 512 runs ring_step_wide (wave pairs split d).
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<64> {
-  static constexpr int BN = 64, NW = 8, WPE = 2;
+  static constexpr int BN = 64, NW = 8, NB = 1, WPE = 2;
   static constexpr bool DMA_K = false;
 };
 template <>
 struct Cfg<128> {
-  static constexpr int BN = 64, NW = 8, WPE = 2;
+  static constexpr int BN = 64, NW = 8, NB = 1, WPE = 2;
   static constexpr bool DMA_K = false;
 };
 template <>
 struct Cfg<512> {
-  static constexpr int BN = 32, NW = 4, WPE = 1;
+  static constexpr int BN = 32, NW = 4, NB = 1, WPE = 1;
   static constexpr bool DMA_K = true;
 };
 constexpr int kWideHalf = 256;   // head_dim 512: each wave of a pair owns half of d
@@ -260,22 +260,24 @@ __device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
   }
 }
 
-// S^T = K Q^T for the keys of a staged tile, in 32-key blocks.
-template <int D>
-__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[D / 16],
-                                        f32x16_t (&sacc)[Cfg<D>::BN / 32]) {
+// S^T = K Q^T for the keys of a staged tile, in 32-key blocks, for the NB
+// 32-row blocks of the wave: every K fragment read from LDS feeds NB MFMAs.
+template <int D, int NB>
+__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[NB][D / 16],
+                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, hf = lane >> 5;
 #pragma unroll
   for (int mb = 0; mb < Cfg<D>::BN / 32; ++mb) {
     const int key = mb * 32 + qi;
-    const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((hf ^ k_swizzle<D>(key)) * 8)]);
-    sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0f, qf[0], f32x16_t{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 1; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks) {
       const int ch = ks * 2 + hf;
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
-      sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[mb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        sacc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], ks == 0 ? f32x16_t{} : sacc[nb][mb],
+                                                              0, 0, 0);
     }
   }
 }
@@ -296,9 +298,10 @@ __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(C
 void ring_step_mfma(SeqTable tab, StepArgs a) {
   constexpr int BN = Cfg<D>::BN;
   constexpr int NW = Cfg<D>::NW;
+  constexpr int NB = Cfg<D>::NB;                // 32-row blocks per wave
   constexpr int MB = BN / 32;                   // 32-key blocks per tile
   constexpr int PKS = BN / 16;                  // 16-key MFMA k-steps of the PV product
-  constexpr int BM = 32 * NW / HG;              // query rows per workgroup
+  constexpr int BM = 32 * NB * NW / HG;         // query rows per workgroup
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
   constexpr int VS = kVStrideOf<D>;
@@ -331,7 +334,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   const int h = hg * HG + (wave % HG);
   const int rep = a.n_hq / a.n_kv;
   const int g = h / rep;
-  const int wrow0 = tile * BM + (wave / HG) * 32;           // wave's first row inside the chunk
+  const int wrow0 = tile * BM + (wave / HG) * 32 * NB;      // wave's first row inside the chunk
   const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
 
   // key segments that are not empty, the tail key chunk first
@@ -346,54 +349,60 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   sg.end[1] = sg.diag[1] ? wg_row_end : c;
   sg.n0 = (sg.end[0] + BN - 1) / BN;
 
-  const int row = wrow0 + qi;
-  const bool row_ok = row < c;
-  const int64_t grow = qrow0 + row;   // local row index in the rank's buffer
-  float *mptr = a.m + (grow * a.n_hq + h);
-  float *dptr = a.den + (grow * a.n_hq + h);
-  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D;
+  int row[NB];
+  bool row_ok[NB];
+  int64_t grow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    row[nb] = wrow0 + nb * 32 + qi;
+    row_ok[nb] = row[nb] < c;
+    grow[nb] = qrow0 + row[nb];   // local row index in the rank's buffer
+  }
 
   if (nseg == 0) {
     // every row of this tile sees no key: the identity (unchanged when accumulating)
-    if (!a.accumulate && row_ok) {
-      if (hf == 0) store_stats(mptr, dptr, kNegInf, 0.f);
+    if (!a.accumulate) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int nb = 0; nb < NB; ++nb) {
+        if (!row_ok[nb]) continue;
+        if (hf == 0) store_stats(a.m + grow[nb] * a.n_hq + h, a.den + grow[nb] * a.n_hq + h, kNegInf, 0.f);
+        float *nptr = a.num + (grow[nb] * a.n_hq + h) * (int64_t)D;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = z;
-        }
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
     return;
   }
   const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + BN - 1) / BN : 0);
 
-  // Q fragment: B operand of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
+  // Q fragments: B operands of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
-  bf16x8_t qf[KS];
-  {
-    const __bf16 *qp = qbase + (grow * a.n_hq + h) * (int64_t)D + 8 * hf;
+  bf16x8_t qf[NB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (row_ok) {
-        qf[ks] = *reinterpret_cast<const bf16x8_t *>(qp + ks * 16);
-      } else {
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        qf[ks] = __builtin_bit_cast(bf16x8_t, z);
-      }
-    }
+  for (int nb = 0; nb < NB; ++nb) {
+    const __bf16 *qp = qbase + (grow[nb] * a.n_hq + h) * (int64_t)D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[nb][ks] = row_ok[nb] ? *reinterpret_cast<const bf16x8_t *>(qp + ks * 16)
+                              : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
   }
 
   const float sl2 = a.scale * kLog2e;
   const float thr = kRescaleLog2 / sl2;   // rescale threshold in raw-score units
-  float m_ref = kNegInf;   // reference max of raw scores q.k (numerator and denominator are relative to it)
-  float l_run = 0.f;       // this lane's share of the denominator
-  f32x16_t oacc[DB];
+  float m_ref[NB], l_run[NB];             // reference max of raw scores; this lane's share of the denominator
+  f32x16_t oacc[NB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int nb = 0; nb < NB; ++nb) {
+    m_ref[nb] = kNegInf;
+    l_run[nb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[nb][db][r] = 0.f;
+  }
 
   const char *kblock = reinterpret_cast<const char *>(a.k);
   const char *vblock = reinterpret_cast<const char *>(a.v);
@@ -422,8 +431,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
-  f32x16_t snext[MB];
-  qk_tile<D>(Ks[0], qf, snext);
+  f32x16_t snext[NB][MB];
+  qk_tile<D, NB>(Ks[0], qf, snext);
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -446,66 +455,90 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
     }
 
-    f32x16_t sacc[MB];
+    f32x16_t sacc[NB][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) sacc[mb] = snext[mb];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sacc[nb][mb] = snext[nb][mb];
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = (kk < kend) && (!diag || kk <= row);
-          if (!vis) sacc[mb][r] = kNegInf;
-        }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = k0 + mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool vis = (kk < kend) && (!diag || kk <= row[nb]);
+            if (!vis) sacc[nb][mb][r] = kNegInf;
+          }
     }
 
     // ---- online softmax (lane = query column; keys split over the two halves)
-    float mx = kNegInf;
+    float mx[NB];
+    bool grows = false;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float x = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__any(mx > m_ref + thr)) {
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[nb][mb][r]);
+      mx[nb] = fmaxf(x, __shfl_xor(x, 32));
+      grows |= mx[nb] > m_ref[nb] + thr;
+    }
+    if (__any(grows)) {
       // the max grew past the threshold for some query of this wave: move every
       // lane's reference to its current max (exact rescale)
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
-      l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int nb = 0; nb < NB; ++nb) {
+        const float m_new = fmaxf(m_ref[nb], mx[nb]);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref[nb] - m_new) * sl2);
+        l_run[nb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_ref = m_new;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][db][r] *= alpha;
+        m_ref[nb] = m_new;
+      }
     }
-    const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+    float mref[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mref[nb] = (m_ref[nb] == kNegInf) ? 0.f : m_ref[nb] * sl2;
 
     // ---- one scheduling region: QK^T of the next tile (matrix cores) with this
     // tile's exponentials (vector ALUs), then this tile's PV product
-    qk_tile<D>(Ks[cur ^ 1], qf, snext);
-    uint32_t pk[MB][8];
+    qk_tile<D, NB>(Ks[cur ^ 1], qf, snext);
+    uint32_t pk[NB][MB][8];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(fmaf(sacc[mb][r], sl2, -mref));
-        const float p1 = exp2_fast(fmaf(sacc[mb][r + 1], sl2, -mref));
-        pk[mb][r >> 1] = pack_bf16x2(p0, p1);
-        // denominator from the same rounded values the PV product uses
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[mb][r >> 1]), ones, l_run, false);
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2_fast(fmaf(sacc[nb][mb][r], sl2, -mref[nb]));
+          const float p1 = exp2_fast(fmaf(sacc[nb][mb][r + 1], sl2, -mref[nb]));
+          pk[nb][mb][r >> 1] = pack_bf16x2(p0, p1);
+          // denominator from the same rounded values the PV product uses
+          l_run[nb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[nb][mb][r >> 1]), ones,
+                                                      l_run[nb], false);
+        }
     const __bf16 *Vc = Vt[cur];
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
       const int mb = ks >> 1;
       const int base = (ks & 1) * 4;
-      u32x4_t pw = {pk[mb][base], pk[mb][base + 1], pk[mb][base + 2], pk[mb][base + 3]};
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+      bf16x8_t pf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        u32x4_t pw = {pk[nb][mb][base], pk[nb][mb][base + 1], pk[nb][mb][base + 2], pk[nb][mb][base + 3]};
+        pf[nb] = __builtin_bit_cast(bf16x8_t, pw);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * VS + ks * 16 + 8 * hf]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], oacc[nb][db], 0, 0, 0);
       }
     }
 
@@ -517,31 +550,38 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   }
 
   // ---- epilogue: natural-log max, full denominator, optional merge, store
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  const float m_nat = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
-  float w_old = 0.f, w_new = 1.f, m_out = m_nat;
-  if (a.accumulate) {
-    const float m_old = *mptr;
-    merge_weights(m_old, m_nat, m_out, w_old, w_new);
-    const float d_old = *dptr;
-    const float d_out = w_old * d_old + w_new * l_tot;
-    if (hf == 0) store_stats(mptr, dptr, m_out, d_out);
-  } else {
-    if (hf == 0) store_stats(mptr, dptr, m_nat, l_tot);
-  }
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
-      f32x4_t o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
-      if (a.accumulate) {
-        const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
-        o = old * w_old + o * w_new;
-      }
-      *reinterpret_cast<f32x4_t *>(p) = o;
+  for (int nb = 0; nb < NB; ++nb) {
+    const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32);
+    if (!row_ok[nb]) continue;
+    float *mptr = a.m + (grow[nb] * a.n_hq + h);
+    float *dptr = a.den + (grow[nb] * a.n_hq + h);
+    float *nptr = a.num + (grow[nb] * a.n_hq + h) * (int64_t)D;
+    const float m_nat = (m_ref[nb] == kNegInf) ? kNegInf : m_ref[nb] * a.scale;
+    float w_old = 0.f, w_new = 1.f, m_out = m_nat;
+    if (a.accumulate) {
+      const float m_old = *mptr;
+      merge_weights(m_old, m_nat, m_out, w_old, w_new);
+      const float d_old = *dptr;
+      const float d_out = w_old * d_old + w_new * l_tot;
+      if (hf == 0) store_stats(mptr, dptr, m_out, d_out);
+    } else {
+      if (hf == 0) store_stats(mptr, dptr, m_nat, l_tot);
     }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
+        f32x4_t o = {oacc[nb][db][4 * g4], oacc[nb][db][4 * g4 + 1], oacc[nb][db][4 * g4 + 2],
+                     oacc[nb][db][4 * g4 + 3]};
+        if (a.accumulate) {
+          const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
+          o = old * w_old + o * w_new;
+        }
+        *reinterpret_cast<f32x4_t *>(p) = o;
+      }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -970,7 +1010,7 @@ bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || 
 int rows_per_unit(int dtype, int d, int rep) {
   if (!use_mfma(dtype, d)) return 1;
   if (d == 512) return 32 * (Cfg<512>::NW / 2) / pick_hg_d(512, rep);
-  return 32 * Cfg<128>::NW / pick_hg(rep);
+  return 32 * Cfg<128>::NB * Cfg<128>::NW / pick_hg(rep);
 }
 
 hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
