@@ -43,7 +43,11 @@ struct Raw16;   // 8 elements as raw words
 template <>
 struct Raw16<__bf16> {
   u32x4_t w;
-  __device__ __forceinline__ void load(const __bf16 *p) { w = *reinterpret_cast<const u32x4_t *>(p); }
+  // K and V are streamed once: non-temporal loads keep them from displacing
+  // other cached data
+  __device__ __forceinline__ void load(const __bf16 *p) {
+    w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  }
   __device__ __forceinline__ void zero() { w = u32x4_t{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t x = w[e >> 1];
@@ -54,8 +58,8 @@ template <>
 struct Raw16<float> {
   f32x4_t a, b;
   __device__ __forceinline__ void load(const float *p) {
-    a = *reinterpret_cast<const f32x4_t *>(p);
-    b = *reinterpret_cast<const f32x4_t *>(p + 4);
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p + 4));
   }
   __device__ __forceinline__ void zero() { a = f32x4_t{0.f, 0.f, 0.f, 0.f}; b = a; }
   __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
