@@ -31,6 +31,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x[lane], x[lane ^ 32]) in every lane: v_permlane32_swap exchanges the two
+// 32-lane halves of a wave register to register, without a round trip through LDS.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Element loads of an input row: 8 consecutive elements widened to fp32.
 template <typename T>
 struct Elem;

@@ -14,13 +14,14 @@
 // Kernels
 //   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 8 waves (two per
 //       SIMD) owns 32*8/HG query rows x HG query heads of one kv group; K and V
-//       tiles of 64 keys are staged in double-buffered LDS (the next tile's global
-//       loads are in flight while the current one computes) and shared by the 8
-//       waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
+//       tiles of 64 keys are staged in double-buffered LDS (K copied straight from
+//       HBM into LDS, V transposed through registers; the next tiles' loads are in
+//       flight while the current one computes) and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
 //       every lane owns one query column of both products and the softmax needs a
 //       single cross-lane exchange per tile.
-//   ring_step_generic<T, D>  fp32 (and bf16 head_dim 512): one workgroup per
-//       (query row, query head), fp32 arithmetic throughout.
+//   ring_step_wide<HG>  bf16, head_dim 512: wave pairs split d (below).
+//   ring_step_generic<T, D>  fp32: one workgroup per (query row, query head),
+//       fp32 arithmetic throughout.
 #include "kernels.h"
 
 namespace cpattn {
@@ -68,27 +69,23 @@ __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, f
 // ----------------------------------------------------------------------------
 
 // Per head_dim configuration: keys per tile (BN), waves per workgroup (NW),
-// 32-row blocks per wave (NB) and whether K goes to LDS by buffer-to-LDS copies
-// (no staging registers) or through registers. head_dim 64/128: 8 waves, two
-// per SIMD, so one wave's MFMAs overlap the other's softmax and latencies
-// (a wave per SIMD with two row blocks halves LDS reads per MFMA but measured
-// half the speed). head_dim 512 runs ring_step_wide (wave pairs split d).
+// 32-row blocks per wave (NB) and waves per SIMD (WPE). head_dim 64/128: 8
+// waves, two per SIMD, so one wave's MFMAs overlap the other's softmax and
+// latencies (a wave per SIMD with two row blocks halves LDS reads per MFMA but
+// measured half the speed). head_dim 512 runs ring_step_wide (wave pairs split d).
 template <int D>
 struct Cfg;
 template <>
 struct Cfg<64> {
   static constexpr int BN = 64, NW = 8, NB = 1, WPE = 2;
-  static constexpr bool DMA_K = false;
 };
 template <>
 struct Cfg<128> {
   static constexpr int BN = 64, NW = 8, NB = 1, WPE = 2;
-  static constexpr bool DMA_K = false;
 };
 template <>
 struct Cfg<512> {
   static constexpr int BN = 32, NW = 4, NB = 1, WPE = 1;
-  static constexpr bool DMA_K = true;
 };
 constexpr int kWideHalf = 256;   // head_dim 512: each wave of a pair owns half of d
 template <int D>
@@ -117,51 +114,40 @@ __device__ __forceinline__ int v_slot(int key) {
 // Per-thread byte offsets (relative to the first key row of a tile) of the K
 // and V staging loads; a thread without a share gets an offset past any tile,
 // which the buffer range check turns into zeros.
-//   K through registers: chunk x = tid + i*threads -> (key x / KCH, chunk x % KCH),
-//     consecutive lanes read consecutive 16-byte chunks of a row.
-//   K straight into LDS: lane L of a wave writes bytes [16L, 16L+16) of the 1 KB
-//     chunk the wave names, so lane L loads the global chunk that belongs at that
-//     position of the swizzled tile.
+//   K goes straight into LDS: lane L of a wave writes bytes [16L, 16L+16) of the
+//     1 KB chunk the wave names, so lane L loads the global chunk that belongs at
+//     that position of the swizzled tile.
 //   V (transposed on the way into LDS, so through registers): lane -> key pair
 //     tid % (BN/2) and chunk tid / (BN/2) (+ threads/(BN/2) per pass), so lanes
 //     of a wave write distinct banks of the transposed tile.
 template <int D>
 struct StageMap {
   static constexpr int BN = Cfg<D>::BN, T = kThreadsOf<D>, KCH = D / 8, P2 = BN / 2;
-  static constexpr int KN = Cfg<D>::DMA_K ? (BN * D * 2 / 1024) / Cfg<D>::NW : (BN * KCH + T - 1) / T;
+  static constexpr int KN = (BN * D * 2 / 1024) / Cfg<D>::NW;   // 1 KB K chunks per wave
   static constexpr int VN = (P2 * KCH + T - 1) / T;
+  static_assert(KN * 1024 * Cfg<D>::NW == BN * D * 2, "K tile must split into whole 1 KB chunks per wave");
   uint32_t k[KN];
   uint32_t v[VN][2];
 };
 
 constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
-constexpr int32_t kBufferWord3 = 0x00020000;   // raw buffer resource word 3 on gfx9
-constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer resource word 3 on gfx9
+constexpr int kWaitVmcnt0 = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <int D>
 __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   using M = StageMap<D>;
   StageMap<D> o;
   const int tid = threadIdx.x;
-  if constexpr (Cfg<D>::DMA_K) {
-    constexpr int ROWS_PER_KB = 1024 / (D * 2);
-    const int wave = tid >> 6, lane = tid & 63;
+  constexpr int ROWS_PER_KB = 1024 / (D * 2);
+  const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int i = 0; i < M::KN; ++i) {
-      const int q = wave * M::KN + i;                    // 1 KB chunk of the tile
-      const int key = q * ROWS_PER_KB + lane / M::KCH;
-      const int pc = lane % M::KCH;                      // physical chunk in the LDS row
-      const int ch = pc ^ k_swizzle<D>(key);             // logical chunk it holds
-      o.k[i] = key * row_bytes + (uint32_t)(g * D * 2 + ch * 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < M::KN; ++i) {
-      const int x = tid + i * M::T;
-      const int key = x / M::KCH;
-      const int ch = x - key * M::KCH;
-      o.k[i] = (x < M::BN * M::KCH) ? key * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
-    }
+  for (int i = 0; i < M::KN; ++i) {
+    const int q = wave * M::KN + i;                    // 1 KB chunk of the tile
+    const int key = q * ROWS_PER_KB + lane / M::KCH;
+    const int pc = lane % M::KCH;                      // physical chunk in the LDS row
+    const int ch = pc ^ k_swizzle<D>(key);             // logical chunk it holds
+    o.k[i] = key * row_bytes + (uint32_t)(g * D * 2 + ch * 16);
   }
   const int kp = tid % M::P2;
 #pragma unroll
@@ -174,58 +160,47 @@ __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   return o;
 }
 
+// Buffer resource of a tile: base at key row `row`, loads at or past
+// rows_left * row_bytes return zeros.
+__device__ __forceinline__ u32x4_t tile_words(const char *block, int64_t row, int rows_left, uint32_t row_bytes) {
+  const int64_t lim = (int64_t)rows_left * row_bytes;
+  const uint32_t nrec = (uint32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
+  const uint64_t base = (uint64_t)(block + row * (int64_t)row_bytes);
+  return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, kBufferWord3};
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *block, int64_t row, int rows_left,
                                                            uint32_t row_bytes) {
   const int64_t lim = (int64_t)rows_left * row_bytes;
   const int32_t nrec = (int32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
   return __builtin_amdgcn_make_buffer_rsrc((void *)(block + row * (int64_t)row_bytes), (short)0, nrec,
-                                           kBufferWord3);
+                                           (int32_t)kBufferWord3);
 }
 
-template <int D>
-struct KRegs {
-  u32x4_t x[Cfg<D>::DMA_K ? 1 : StageMap<D>::KN];
-};
 template <int D>
 struct VRegs {
   u32x4_t x[StageMap<D>::VN][2];
 };
 
-// Starts the copy of K tile into its LDS buffer: through registers (load_k, then
-// store_k) or straight into LDS (complete once vmcnt reaches zero).
+// Starts the copy of a K tile straight into its LDS buffer (buffer_load ... lds,
+// 16 bytes per lane, M0 = the wave's 1 KB destination). The copy is written as
+// inline assembly on purpose: the compiler tracks its own buffer-to-LDS copies
+// and, unable to tell LDS ranges apart, makes the first LDS read after one wait
+// for every outstanding vector load, which would expose the whole load latency
+// at the top of each tile. The kernels wait for these copies themselves
+// (vmcnt(0) before the barrier that publishes the tile).
 template <int D>
-__device__ __forceinline__ void load_k(KRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs, __bf16 *Ks) {
-  if constexpr (Cfg<D>::DMA_K) {
+__device__ __forceinline__ void load_k(const StageMap<D> &o, u32x4_t rsrc, __bf16 *Ks) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < StageMap<D>::KN; ++i) {
-      __bf16 *dst = Ks + (wave * StageMap<D>::KN + i) * 512;   // 1 KB chunk
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16, o.k[i], 0,
-                                               0, 0);
-    }
+  for (int i = 0; i < StageMap<D>::KN; ++i) {
+    __bf16 *dst = Ks + (wave * StageMap<D>::KN + i) * 512;   // 1 KB chunk
+    const uint32_t lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)dst);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(o.k[i]), "s"(rsrc), "{m0}"(lds));
+  }
 #endif
-  } else {
-#pragma unroll
-    for (int i = 0; i < StageMap<D>::KN; ++i)
-      r.x[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.k[i], 0, 0));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_k(const KRegs<D> &r, __bf16 *Ks) {
-  if constexpr (!Cfg<D>::DMA_K) {
-    using M = StageMap<D>;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < M::KN; ++i) {
-      const int x = tid + i * M::T;
-      const int key = x / M::KCH;
-      const int ch = x - key * M::KCH;
-      if (x < M::BN * M::KCH)
-        *reinterpret_cast<u32x4_t *>(&Ks[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]) = r.x[i];
-    }
-  }
 }
 
 template <int D>
@@ -257,6 +232,24 @@ __device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
         *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VS + slot]) = hi;
       }
     }
+  }
+}
+
+// Work unit and head group of a workgroup. When the head groups come in
+// multiples of 8, the grid walks them XCD-major: workgroup b runs on XCD b % 8
+// and takes head group (b % 8) + 8 * ((b / 8) / units), so the workgroups
+// resident on one XCD at a time share a head group, and with it the K and V
+// tiles in that XCD's L2. Otherwise unit-major, head group fastest.
+__device__ __forceinline__ void unit_and_group(int n_hg, int &unit, int &hg) {
+  const int b = blockIdx.x;
+  if ((n_hg & 7) == 0) {
+    const int units = gridDim.x / n_hg;
+    const int j = b >> 3;
+    unit = j % units;
+    hg = (b & 7) + 8 * (j / units);
+  } else {
+    unit = b / n_hg;
+    hg = b - unit * n_hg;
   }
 }
 
@@ -318,8 +311,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   const int hf = lane >> 5;
 
   const int n_hg = a.n_hq / HG;
-  const int unit = blockIdx.x / n_hg;
-  const int hg = blockIdx.x - unit * n_hg;
+  int unit, hg;
+  unit_and_group(n_hg, unit, hg);
   const int si = find_seq(tab, unit);
   const int c = tab.c[si];
   const int nt = (c + BM - 1) / BM;
@@ -416,16 +409,13 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   // it run on the vector ALUs, then V of tile it. A tile that lies entirely in
   // the future of a wave's rows is masked to -inf and contributes zeros.
   {
-    KRegs<D> kr;
     VRegs<D> vr;
-    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
+    load_k<D>(smap, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
     load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
-    store_k<D>(kr, Ks[0]);
     store_v<D>(vr, Vt[0]);
     if (ntiles > 1) {
       const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
-      store_k<D>(kr, Ks[1]);
+      load_k<D>(smap, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -442,13 +432,12 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     const bool diag = sg.diag[sc];
 
     // prefetch: K of tile it+2 (into the LDS buffer of K of tile it, read in the
-    // previous iteration, or into registers) and V of tile it+1 into registers
-    KRegs<D> kr;
+    // previous iteration) and V of tile it+1 into registers
     VRegs<D> vr;
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
+      load_k<D>(smap, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
     }
     if (pv1) {
       const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
@@ -483,7 +472,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[nb][mb][r]);
-      mx[nb] = fmaxf(x, __shfl_xor(x, 32));
+      mx[nb] = max_across_halves(x);
       grows |= mx[nb] > m_ref[nb] + thr;
     }
     if (__any(grows)) {
@@ -543,9 +532,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     }
 
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
-    if (pk2) store_k<D>(kr, Ks[cur]);
     if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
-    if constexpr (Cfg<D>::DMA_K) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
@@ -620,8 +608,8 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int pair = wave >> 1, dh = wave & 1;
 
   const int n_hg = a.n_hq / HG;
-  const int unit = blockIdx.x / n_hg;
-  const int hg = blockIdx.x - unit * n_hg;
+  int unit, hg;
+  unit_and_group(n_hg, unit, hg);
   const int si = find_seq(tab, unit);
   const int c = tab.c[si];
   const int nt = (c + BM - 1) / BM;
@@ -707,14 +695,13 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   };
 
   {
-    KRegs<D> kr;
     VRegs<D> vr;
-    load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
+    load_k<D>(smap, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
     load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
     store_v<D>(vr, Vt[0]);
     if (ntiles > 1) {
       const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
+      load_k<D>(smap, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -731,12 +718,11 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    KRegs<D> kr;
     VRegs<D> vr;
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_k<D>(kr, smap, tile_rsrc(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
+      load_k<D>(smap, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
     }
     if (pv1) {
       const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
@@ -758,7 +744,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_across_halves(mx);
     if (__any(mx > m_ref + thr)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
