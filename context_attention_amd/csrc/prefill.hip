@@ -93,6 +93,30 @@ constexpr int kThreadsOf = 64 * Cfg<D>::NW;
 template <int D>
 constexpr int kVStrideOf = Cfg<D>::BN + 8;   // padded row of the transposed V tile (bf16 elements)
 
+// Transposed V tile in LDS: row = head-dim index, slot = key position (v_slot).
+// head_dim 64/128: rows padded to kVStrideOf elements. head_dim 512 (32-key
+// rows of 16 words, no padding): row r lives in quarter (r & 3) ^ ((r >> 3) & 3)
+// of the 256-byte line r / 4, and its 16-byte word groups are XOR-permuted by
+// g(r) = ((r >> 1) ^ (r >> 3)) & 1 | ((r >> 2) & 1) << 1. With this placement
+// the transposing stores (64 lanes: 16 key pairs x 4 rows 8 apart) and the
+// 16-byte PV reads (consecutive rows) both touch distinct banks, whether the
+// LDS serves 32 or 64 banks per cycle.
+template <int D>
+constexpr int kVTileOf = (D == 512) ? D * Cfg<D>::BN : D * kVStrideOf<D>;
+template <int D>
+constexpr int kVRowStepOf = (D == 512) ? Cfg<D>::BN : kVStrideOf<D>;   // element step of 1 row (32-row aligned moves)
+template <int D>
+__device__ __forceinline__ int vt_index(int row, int slot) {
+  if constexpr (D == 512) {
+    static_assert(Cfg<D>::BN == 32, "the head_dim 512 V swizzle assumes 32-key rows");
+    const int q = (row & 3) ^ ((row >> 3) & 3);
+    const int g = (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
+    return 2 * (64 * (row >> 2) + 16 * q + ((slot >> 1) ^ (4 * g))) + (slot & 1);
+  } else {
+    return row * kVStrideOf<D> + slot;
+  }
+}
+
 // Rescale threshold of the running max in the exp2 domain: the numerator and
 // denominator are only rescaled when the max grows by more than 2^8, so
 // exp2(s - m_ref) stays below 256.
@@ -215,7 +239,6 @@ __device__ __forceinline__ void load_v(VRegs<D> &r, const StageMap<D> &o, __amdg
 template <int D>
 __device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
   using M = StageMap<D>;
-  constexpr int VS = kVStrideOf<D>;
   const int tid = threadIdx.x;
   const int kp = tid % M::P2;
   const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
@@ -228,8 +251,8 @@ __device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
         const int d0 = ch * 8 + 2 * i;
         const uint32_t lo = (r.x[j][0][i] & 0xFFFFu) | (r.x[j][1][i] << 16);
         const uint32_t hi = (r.x[j][0][i] >> 16) | (r.x[j][1][i] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t *>(&Vt[d0 * VS + slot]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VS + slot]) = hi;
+        *reinterpret_cast<uint32_t *>(&Vt[vt_index<D>(d0, slot)]) = lo;
+        *reinterpret_cast<uint32_t *>(&Vt[vt_index<D>(d0 + 1, slot)]) = hi;
       }
     }
   }
@@ -297,9 +320,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   constexpr int BM = 32 * NB * NW / HG;         // query rows per workgroup
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
-  constexpr int VS = kVStrideOf<D>;
   constexpr int KSZ = BN * D;                   // K tile (bf16 elements)
-  constexpr int VSZ = D * VS;                   // transposed V tile
+  constexpr int VSZ = kVTileOf<D>;             // transposed V tile
 
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
@@ -524,7 +546,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(db * 32 + qi) * VS + ks * 16 + 8 * hf]);
+        const bf16x8_t vf =
+            *reinterpret_cast<const bf16x8_t *>(&Vc[vt_index<D>(qi, ks * 16 + 8 * hf) + db * 32 * kVRowStepOf<D>]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], oacc[nb][db], 0, 0, 0);
@@ -583,6 +606,26 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 // same softmax; the PV product then fills each wave's half of the output. Keys
 // come in 32-key tiles; K is copied straight into LDS, V is transposed through
 // registers.
+__device__ __forceinline__ void put_scores(f32x4_t (*x)[64], const f32x16_t &s) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) x[g][lane] = f32x4_t{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
+}
+
+__device__ __forceinline__ f32x16_t get_scores(const f32x4_t (*x)[64]) {
+  const int lane = threadIdx.x & 63;
+  f32x16_t s;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4_t t = x[g][lane];
+    s[4 * g] = t[0];
+    s[4 * g + 1] = t[1];
+    s[4 * g + 2] = t[2];
+    s[4 * g + 3] = t[3];
+  }
+  return s;
+}
+
 template <int HG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ring_step_wide(SeqTable tab, StepArgs a) {
@@ -592,13 +635,14 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   constexpr int BM = 32 * NP / HG;              // query rows per workgroup
   constexpr int KSH = kWideHalf / 16;           // QK^T k-steps over one half of d
   constexpr int DBH = kWideHalf / 32;           // output d blocks of one half
-  constexpr int VS = kVStrideOf<D>;
   constexpr int KSZ = BN * D;
-  constexpr int VSZ = D * VS;
+  constexpr int VSZ = kVTileOf<D>;
 
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
-  __shared__ __attribute__((aligned(16))) f32x16_t Sx[Cfg<D>::NW][64];   // partial scores, one tile per wave
+  // partial scores, one 32 x 32 tile per wave, stored [wave][quarter][lane] so
+  // that every 16-byte access of a wave covers 1 KB of consecutive banks
+  __shared__ __attribute__((aligned(16))) f32x4_t Sx[Cfg<D>::NW][4][64];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -708,7 +752,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   __syncthreads();
   f32x16_t spart;
   qk_half(Ks[0], spart);
-  Sx[wave][lane] = spart;
+  put_scores(Sx[wave], spart);
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
@@ -730,7 +774,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     }
 
     // full scores of tile it = own partial + the partner's partial
-    f32x16_t sacc = spart + Sx[wave ^ 1][lane];
+    f32x16_t sacc = spart + get_scores(Sx[wave ^ 1]);
     __syncthreads();   // both partials read before either is overwritten
 
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
@@ -775,12 +819,13 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
 #pragma unroll
       for (int db = 0; db < DBH; ++db) {
         const int d0 = dh * kWideHalf + db * 32;
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vc[(d0 + qi) * VS + ks * 16 + 8 * hf]);
+        const bf16x8_t vf =
+            *reinterpret_cast<const bf16x8_t *>(&Vc[vt_index<D>(qi, ks * 16 + 8 * hf) + d0 * kVRowStepOf<D>]);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
     }
 
-    Sx[wave][lane] = spart;
+    put_scores(Sx[wave], spart);
     if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
