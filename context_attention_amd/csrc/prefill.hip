@@ -14,9 +14,9 @@
 // Kernels
 //   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 8 waves (two per
 //       SIMD) owns 32*8/HG query rows x HG query heads of one kv group; K and V
-//       tiles of 64 keys are staged in double-buffered LDS (K copied straight from
-//       HBM into LDS, V transposed through registers; the next tiles' loads are in
-//       flight while the current one computes) and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
+//       tiles of 64 keys are copied straight from HBM into double-buffered LDS
+//       (the next tiles' copies are in flight while the current one computes)
+//       and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
 //       every lane owns one query column of both products and the softmax needs a
 //       single cross-lane exchange per tile.
 //   ring_step_wide<HG>  bf16, head_dim 512: wave pairs split d (below).
@@ -90,71 +90,42 @@ struct Cfg<512> {
 constexpr int kWideHalf = 256;   // head_dim 512: each wave of a pair owns half of d
 template <int D>
 constexpr int kThreadsOf = 64 * Cfg<D>::NW;
-template <int D>
-constexpr int kVStrideOf = Cfg<D>::BN + 8;   // padded row of the transposed V tile (bf16 elements)
-
-// Transposed V tile in LDS: row = head-dim index, slot = key position (v_slot).
-// head_dim 64/128: rows padded to kVStrideOf elements. head_dim 512 (32-key
-// rows of 16 words, no padding): row r lives in quarter (r & 3) ^ ((r >> 3) & 3)
-// of the 256-byte line r / 4, and its 16-byte word groups are XOR-permuted by
-// g(r) = ((r >> 1) ^ (r >> 3)) & 1 | ((r >> 2) & 1) << 1. With this placement
-// the transposing stores (64 lanes: 16 key pairs x 4 rows 8 apart) and the
-// 16-byte PV reads (consecutive rows) both touch distinct banks, whether the
-// LDS serves 32 or 64 banks per cycle.
-template <int D>
-constexpr int kVTileOf = (D == 512) ? D * Cfg<D>::BN : D * kVStrideOf<D>;
-template <int D>
-constexpr int kVRowStepOf = (D == 512) ? Cfg<D>::BN : kVStrideOf<D>;   // element step of 1 row (32-row aligned moves)
-template <int D>
-__device__ __forceinline__ int vt_index(int row, int slot) {
-  if constexpr (D == 512) {
-    static_assert(Cfg<D>::BN == 32, "the head_dim 512 V swizzle assumes 32-key rows");
-    const int q = (row & 3) ^ ((row >> 3) & 3);
-    const int g = (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1);
-    return 2 * (64 * (row >> 2) + 16 * q + ((slot >> 1) ^ (4 * g))) + (slot & 1);
-  } else {
-    return row * kVStrideOf<D> + slot;
-  }
-}
-
 // Rescale threshold of the running max in the exp2 domain: the numerator and
 // denominator are only rescaled when the max grows by more than 2^8, so
 // exp2(s - m_ref) stays below 256.
 constexpr float kRescaleLog2 = 8.0f;
 
+// K and V tiles sit in LDS as they are in HBM, [key][d] bf16, with the 16-byte
+// chunks of each row permuted (chunk c of row r at position c ^ swizzle(r)).
+//   K: read as the A operand of S^T = K Q^T, 16 bytes of one row per lane, 32
+//     consecutive rows per wave; k_swizzle spreads 16 consecutive rows of one
+//     chunk over 16 distinct bank groups.
+//   V: read transposed by ds_read_b64_tr_b16 (below); a 16-lane group reads 8
+//     bytes from each of 4 consecutive rows, and v_swizzle puts those 4 rows on
+//     disjoint banks whether the LDS serves 32 or 64 banks per cycle.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int row) {
-  // 16-byte chunk permutation of a K row so that 16 lanes reading the same
-  // chunk of 16 consecutive rows hit 16 distinct bank groups.
   return (D == 64) ? ((row >> 1) & 7) : (row & 15);
 }
-
-// Slot of tile key `key` in a row of the transposed V tile: the order in which
-// the MFMA k index walks the keys of the P fragment (see the PV product).
-__device__ __forceinline__ int v_slot(int key) {
-  return (key >> 4) * 16 + ((key >> 2) & 1) * 8 + ((key >> 3) & 1) * 4 + (key & 3);
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) {
+  return (D == 64) ? 2 * (row & 3) : 4 * (row & 1) + 10 * ((row >> 1) & 1);
 }
 
-// Per-thread byte offsets (relative to the first key row of a tile) of the K
-// and V staging loads; a thread without a share gets an offset past any tile,
-// which the buffer range check turns into zeros.
-//   K goes straight into LDS: lane L of a wave writes bytes [16L, 16L+16) of the
-//     1 KB chunk the wave names, so lane L loads the global chunk that belongs at
-//     that position of the swizzled tile.
-//   V (transposed on the way into LDS, so through registers): lane -> key pair
-//     tid % (BN/2) and chunk tid / (BN/2) (+ threads/(BN/2) per pass), so lanes
-//     of a wave write distinct banks of the transposed tile.
+// Per-thread byte offsets (relative to the first key row of a tile) of the
+// buffer-to-LDS copies of a K and a V tile. Lane L of a wave writes bytes
+// [16L, 16L+16) of the 1 KB LDS chunk the wave names, so it loads the global
+// chunk that belongs at that position of the swizzled tile; every copy
+// instruction moves whole rows, which keeps the loads at full line width.
 template <int D>
 struct StageMap {
-  static constexpr int BN = Cfg<D>::BN, T = kThreadsOf<D>, KCH = D / 8, P2 = BN / 2;
-  static constexpr int KN = (BN * D * 2 / 1024) / Cfg<D>::NW;   // 1 KB K chunks per wave
-  static constexpr int VN = (P2 * KCH + T - 1) / T;
-  static_assert(KN * 1024 * Cfg<D>::NW == BN * D * 2, "K tile must split into whole 1 KB chunks per wave");
+  static constexpr int BN = Cfg<D>::BN, KCH = D / 8;
+  static constexpr int KN = (BN * D * 2 / 1024) / Cfg<D>::NW;   // 1 KB chunks per wave and tile
+  static_assert(KN * 1024 * Cfg<D>::NW == BN * D * 2, "a tile must split into whole 1 KB chunks per wave");
   uint32_t k[KN];
-  uint32_t v[VN][2];
+  uint32_t v[KN];
 };
 
-constexpr uint32_t kNoLoad = 0x7FFFFFF0u;
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer resource word 3 on gfx9
 constexpr int kWaitVmcnt0 = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 
@@ -162,24 +133,16 @@ template <int D>
 __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   using M = StageMap<D>;
   StageMap<D> o;
-  const int tid = threadIdx.x;
   constexpr int ROWS_PER_KB = 1024 / (D * 2);
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < M::KN; ++i) {
     const int q = wave * M::KN + i;                    // 1 KB chunk of the tile
     const int key = q * ROWS_PER_KB + lane / M::KCH;
     const int pc = lane % M::KCH;                      // physical chunk in the LDS row
-    const int ch = pc ^ k_swizzle<D>(key);             // logical chunk it holds
-    o.k[i] = key * row_bytes + (uint32_t)(g * D * 2 + ch * 16);
-  }
-  const int kp = tid % M::P2;
-#pragma unroll
-  for (int j = 0; j < M::VN; ++j) {
-    const int ch = tid / M::P2 + j * (M::T / M::P2);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      o.v[j][e] = (ch < M::KCH) ? (2 * kp + e) * row_bytes + (uint32_t)(g * D * 2 + ch * 16) : kNoLoad;
+    const uint32_t base = key * row_bytes + (uint32_t)(g * D * 2);
+    o.k[i] = base + (uint32_t)((pc ^ k_swizzle<D>(key)) * 16);   // logical chunk held there
+    o.v[i] = base + (uint32_t)((pc ^ v_swizzle<D>(key)) * 16);
   }
   return o;
 }
@@ -193,20 +156,7 @@ __device__ __forceinline__ u32x4_t tile_words(const char *block, int64_t row, in
   return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, kBufferWord3};
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *block, int64_t row, int rows_left,
-                                                           uint32_t row_bytes) {
-  const int64_t lim = (int64_t)rows_left * row_bytes;
-  const int32_t nrec = (int32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
-  return __builtin_amdgcn_make_buffer_rsrc((void *)(block + row * (int64_t)row_bytes), (short)0, nrec,
-                                           (int32_t)kBufferWord3);
-}
-
-template <int D>
-struct VRegs {
-  u32x4_t x[StageMap<D>::VN][2];
-};
-
-// Starts the copy of a K tile straight into its LDS buffer (buffer_load ... lds,
+// Starts the copy of a tile straight into its LDS buffer (buffer_load ... lds,
 // 16 bytes per lane, M0 = the wave's 1 KB destination). The copy is written as
 // inline assembly on purpose: the compiler tracks its own buffer-to-LDS copies
 // and, unable to tell LDS ranges apart, makes the first LDS read after one wait
@@ -214,48 +164,48 @@ struct VRegs {
 // at the top of each tile. The kernels wait for these copies themselves
 // (vmcnt(0) before the barrier that publishes the tile).
 template <int D>
-__device__ __forceinline__ void load_k(const StageMap<D> &o, u32x4_t rsrc, __bf16 *Ks) {
+__device__ __forceinline__ void load_tile(const uint32_t (&off)[StageMap<D>::KN], u32x4_t rsrc, __bf16 *dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < StageMap<D>::KN; ++i) {
-    __bf16 *dst = Ks + (wave * StageMap<D>::KN + i) * 512;   // 1 KB chunk
+    __bf16 *chunk = dst + (wave * StageMap<D>::KN + i) * 512;   // 1 KB
     const uint32_t lds =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)dst);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(o.k[i]), "s"(rsrc), "{m0}"(lds));
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)chunk);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rsrc), "{m0}"(lds));
   }
 #endif
 }
 
-template <int D>
-__device__ __forceinline__ void load_v(VRegs<D> &r, const StageMap<D> &o, __amdgpu_buffer_rsrc_t rs) {
-#pragma unroll
-  for (int j = 0; j < StageMap<D>::VN; ++j)
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      r.x[j][e] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o.v[j][e], 0, 0));
-}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
+// A operand of O^T = V^T P^T for k-step ks (16 keys) and the 32 head-dim
+// columns [d0, d0 + 32): lane (m = lane % 32, h = lane / 32) needs V[key][d0 + m]
+// for the keys 16 ks + 4 h + {0..3} (elements 0..3) and 16 ks + 8 + 4 h + {0..3}
+// (elements 4..7), the order in which the S^T accumulator lays out the keys of
+// the P fragment. ds_read_b64_tr_b16 gives lane i of a 16-lane group element e
+// of the 8 bytes addressed by lane 4e + i/4, so when lane j of the group
+// addresses row k0 + j/4 at column c0 + 4 (j % 4), lane i receives
+// V[k0 .. k0 + 3][c0 + i]: one read per 4 keys, the second 8 rows further on.
+// d0 must be a multiple of 32.
 template <int D>
-__device__ __forceinline__ void store_v(const VRegs<D> &r, __bf16 *Vt) {
-  using M = StageMap<D>;
-  const int tid = threadIdx.x;
-  const int kp = tid % M::P2;
-  const int slot = v_slot(2 * kp);   // slots of keys 2kp and 2kp+1 are adjacent
-#pragma unroll
-  for (int j = 0; j < M::VN; ++j) {
-    const int ch = tid / M::P2 + j * (M::T / M::P2);
-    if (ch < M::KCH) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = ch * 8 + 2 * i;
-        const uint32_t lo = (r.x[j][0][i] & 0xFFFFu) | (r.x[j][1][i] << 16);
-        const uint32_t hi = (r.x[j][0][i] >> 16) | (r.x[j][1][i] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t *>(&Vt[vt_index<D>(d0, slot)]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[vt_index<D>(d0 + 1, slot)]) = hi;
-      }
-    }
-  }
+__device__ __forceinline__ bf16x8_t v_fragment(const __bf16 *Vc, int ks, int d0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15;
+  const int row = 16 * ks + 4 * (lane >> 5) + (j >> 2);
+  const int col = d0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int off = row * D + 8 * ((col >> 3) ^ v_swizzle<D>(row)) + (col & 7);   // rows +8 share the swizzle
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const lds_i16x4 *p = (const lds_i16x4 *)(Vc + off);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 2 * D));
+  const i16x4_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+#else
+  (void)Vc; (void)ks; (void)d0;
+  return bf16x8_t{};
+#endif
 }
 
 // Work unit and head group of a workgroup. When the head groups come in
@@ -321,7 +271,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
   constexpr int KSZ = BN * D;                   // K tile (bf16 elements)
-  constexpr int VSZ = kVTileOf<D>;             // transposed V tile
+  constexpr int VSZ = BN * D;                   // V tile
 
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
@@ -431,13 +381,11 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   // it run on the vector ALUs, then V of tile it. A tile that lies entirely in
   // the future of a wave's rows is masked to -inf and contributes zeros.
   {
-    VRegs<D> vr;
-    load_k<D>(smap, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
-    load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
-    store_v<D>(vr, Vt[0]);
+    load_tile<D>(smap.k, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
+    load_tile<D>(smap.v, tile_words(vblock, sg.row[0], sg.end[0], row_bytes), Vt[0]);
     if (ntiles > 1) {
       const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_k<D>(smap, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
+      load_tile<D>(smap.k, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -453,17 +401,16 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    // prefetch: K of tile it+2 (into the LDS buffer of K of tile it, read in the
-    // previous iteration) and V of tile it+1 into registers
-    VRegs<D> vr;
+    // prefetch: K of tile it+2 into the LDS buffer of K of tile it (read in the
+    // previous iteration) and V of tile it+1 into that of V of tile it-1
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_k<D>(smap, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
+      load_tile<D>(smap.k, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
     }
     if (pv1) {
       const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
-      load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
+      load_tile<D>(smap.v, tile_words(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Vt[cur ^ 1]);
     }
 
     f32x16_t sacc[NB][MB];
@@ -546,8 +493,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t vf =
-            *reinterpret_cast<const bf16x8_t *>(&Vc[vt_index<D>(qi, ks * 16 + 8 * hf) + db * 32 * kVRowStepOf<D>]);
+        const bf16x8_t vf = v_fragment<D>(Vc, ks, db * 32);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], oacc[nb][db], 0, 0, 0);
@@ -555,7 +501,6 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     }
 
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
-    if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
@@ -604,8 +549,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 // each wave multiplies its half, the pair exchanges the two partial 32 x 32 score
 // tiles through LDS and both add them, so both hold the full scores and run the
 // same softmax; the PV product then fills each wave's half of the output. Keys
-// come in 32-key tiles; K is copied straight into LDS, V is transposed through
-// registers.
+// come in 32-key tiles copied straight into double-buffered LDS.
 __device__ __forceinline__ void put_scores(f32x4_t (*x)[64], const f32x16_t &s) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -636,7 +580,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   constexpr int KSH = kWideHalf / 16;           // QK^T k-steps over one half of d
   constexpr int DBH = kWideHalf / 32;           // output d blocks of one half
   constexpr int KSZ = BN * D;
-  constexpr int VSZ = kVTileOf<D>;
+  constexpr int VSZ = BN * D;
 
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
@@ -739,13 +683,11 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   };
 
   {
-    VRegs<D> vr;
-    load_k<D>(smap, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
-    load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[0], sg.end[0], row_bytes));
-    store_v<D>(vr, Vt[0]);
+    load_tile<D>(smap.k, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
+    load_tile<D>(smap.v, tile_words(vblock, sg.row[0], sg.end[0], row_bytes), Vt[0]);
     if (ntiles > 1) {
       const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_k<D>(smap, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
+      load_tile<D>(smap.k, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -762,15 +704,14 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    VRegs<D> vr;
     const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
     if (pk2) {
       const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_k<D>(smap, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
+      load_tile<D>(smap.k, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
     }
     if (pv1) {
       const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
-      load_v<D>(vr, smap, tile_rsrc(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes));
+      load_tile<D>(smap.v, tile_words(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Vt[cur ^ 1]);
     }
 
     // full scores of tile it = own partial + the partner's partial
@@ -819,14 +760,12 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
 #pragma unroll
       for (int db = 0; db < DBH; ++db) {
         const int d0 = dh * kWideHalf + db * 32;
-        const bf16x8_t vf =
-            *reinterpret_cast<const bf16x8_t *>(&Vc[vt_index<D>(qi, ks * 16 + 8 * hf) + d0 * kVRowStepOf<D>]);
+        const bf16x8_t vf = v_fragment<D>(Vc, ks, d0);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
     }
 
     put_scores(Sx[wave], spart);
-    if (pv1) store_v<D>(vr, Vt[cur ^ 1]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
