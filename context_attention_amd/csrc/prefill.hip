@@ -390,6 +390,13 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
+  // buffer resource of tile t, or an empty range (the copy then writes zeros and
+  // touches no memory) past the last tile, so the loop body has no branch
+  auto tile_at = [&](const char *blk, int t) {
+    const bool ok = t < ntiles;
+    const int s = sg.seg(t), k = sg.k0(t);
+    return tile_words(blk, ok ? sg.row[s] + k : 0, ok ? sg.end[s] - k : 0, row_bytes);
+  };
 
   f32x16_t snext[NB][MB];
   qk_tile<D, NB>(Ks[0], qf, snext);
@@ -403,15 +410,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
     // prefetch: K of tile it+2 into the LDS buffer of K of tile it (read in the
     // previous iteration) and V of tile it+1 into that of V of tile it-1
-    const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
-    if (pk2) {
-      const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_tile<D>(smap.k, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
-    }
-    if (pv1) {
-      const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
-      load_tile<D>(smap.v, tile_words(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Vt[cur ^ 1]);
-    }
+    load_tile<D>(smap.k, tile_at(kblock, it + 2), Ks[cur]);
+    load_tile<D>(smap.v, tile_at(vblock, it + 1), Vt[cur ^ 1]);
 
     f32x16_t sacc[NB][MB];
 #pragma unroll
@@ -692,6 +692,13 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
+  // buffer resource of tile t, or an empty range (the copy then writes zeros and
+  // touches no memory) past the last tile, so the loop body has no branch
+  auto tile_at = [&](const char *blk, int t) {
+    const bool ok = t < ntiles;
+    const int s = sg.seg(t), k = sg.k0(t);
+    return tile_words(blk, ok ? sg.row[s] + k : 0, ok ? sg.end[s] - k : 0, row_bytes);
+  };
   f32x16_t spart;
   qk_half(Ks[0], spart);
   put_scores(Sx[wave], spart);
@@ -704,15 +711,8 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    const bool pk2 = it + 2 < ntiles, pv1 = it + 1 < ntiles;
-    if (pk2) {
-      const int s2 = sg.seg(it + 2), k2 = sg.k0(it + 2);
-      load_tile<D>(smap.k, tile_words(kblock, sg.row[s2] + k2, sg.end[s2] - k2, row_bytes), Ks[cur]);
-    }
-    if (pv1) {
-      const int s1 = sg.seg(it + 1), k1 = sg.k0(it + 1);
-      load_tile<D>(smap.v, tile_words(vblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Vt[cur ^ 1]);
-    }
+    load_tile<D>(smap.k, tile_at(kblock, it + 2), Ks[cur]);
+    load_tile<D>(smap.v, tile_at(vblock, it + 1), Vt[cur ^ 1]);
 
     // full scores of tile it = own partial + the partner's partial
     f32x16_t sacc = spart + get_scores(Sx[wave ^ 1]);
