@@ -89,12 +89,49 @@ def measured_traffic(kernel):
     return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
 
 
+def overlap_report(ca, synth, torch, pdesc, q0, blocks):
+    """Pass-KV ring with its block transfers on a DMA copy engine beside the
+    ring steps (cpattn_ring_prefill_overlapped, three receive buffers), after
+    the timed steps: the headline rank-0 share (the spec's large-S/cp
+    metamorphic check, < 10% from pure compute) and a middle-band ring (MHA,
+    64 heads, S=16384, cp=8, rank 3; transfer/compute ratio in [0.5, 2])."""
+    ov = ca.overlap
+    comp, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    log("bench: overlap, headline share")
+    x = ov.make_inputs(pdesc, 0, q0, [k for k, _ in blocks], [v for _, v in blocks], n_recv=3)
+    meta = ov.overlap_metamorphic(x, 0, comp, xfer, reps=1)
+    del x
+    log("bench: overlap, middle band")
+    w = synth.PrefillWorkload(name="mha 16384", seqlens=[16384], cp=8, n_hq=64, n_kv=64, head_dim=128,
+                              dtype="bf16", scale_in=0.5, seed=1)
+    S = w.total_tokens
+    full = [synth.tensor_torch(w.seed, t, (S, w.n_hq, w.head_dim), w.scale_in, w.dtype, "cuda")
+            for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)]
+    kb, vb, q3 = [], [], None
+    for j in range(w.cp):
+        idx = torch.from_numpy(ca.balanced_split(w.cu_seqlens, w.cp, j)[0]).to("cuda")
+        kb.append(full[1].index_select(0, idx).contiguous())
+        vb.append(full[2].index_select(0, idx).contiguous())
+        if j == 3:
+            q3 = full[0].index_select(0, idx).contiguous()
+    del full
+    desc = ca.PrefillDesc(cp=w.cp, cu_seqlens=w.cu_seqlens, n_hq=w.n_hq, n_kv=w.n_kv, head_dim=w.head_dim,
+                          dtype=w.dtype, scale=w.softmax_scale)
+    band = ov.overlap_effective(ov.make_inputs(desc, 3, q3, kb, vb, n_recv=3), 0, comp, xfer, reps=5)
+    rnd = lambda d: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items() if k != "workgroups"}
+    return {"transfer": "DMA copy engine", "receive_buffers": 3,
+            "headline_share": rnd(meta),
+            "middle_band": dict(workload="MHA 64 heads, d128, S=16384, cp=8, rank 3", **rnd(band))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the transfer/compute overlap measurements that follow the timed steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -244,7 +281,10 @@ def main():
                          "traffic": measured_traffic("decode_partial")},
         },
     }
-    del blocks, kshards, vshards
+    del kshards, vshards
+    if not args.no_overlap:
+        res["overlap"] = overlap_report(ca, synth, torch, pdesc, q0, blocks)
+    del blocks
     torch.cuda.empty_cache()
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)

@@ -6,7 +6,8 @@ streams. The binding fails loudly when the library has not been built; there
 is no fallback path.
 
 Entry points mirror the C names of include/cpattn.h:
-    balanced_split, ring_step_partial, merge, passq_decode, account
+    balanced_split, ring_step_partial, ring_pass, ring_prefill_overlapped,
+    merge, passq_decode, account
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ import numpy as np
 
 __all__ = [
     "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
-    "balanced_split", "ring_step_partial", "merge", "passq_decode", "passq_workspace_bytes",
+    "balanced_split", "ring_step_partial", "ring_pass", "ring_prefill_overlapped", "merge",
+    "passq_decode", "passq_workspace_bytes",
     "account", "new_partial",
 ]
 
@@ -31,8 +33,9 @@ _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPP
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
 
-EXPORTS = ["cpattn_balanced_split", "cpattn_ring_step_partial", "cpattn_merge",
-           "cpattn_passq_decode", "cpattn_account", "cpattn_version"]
+EXPORTS = ["cpattn_balanced_split", "cpattn_ring_step_partial", "cpattn_ring_pass",
+           "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_passq_decode", "cpattn_account",
+           "cpattn_version"]
 
 
 class CpattnError(RuntimeError):
@@ -96,6 +99,10 @@ def load():
                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.cpattn_ring_step_partial.argtypes = [ctypes.POINTER(_PrefillDesc), i32, i32, vp, vp, vp,
                                              ctypes.POINTER(_Partial), i32, vp]
+    lib.cpattn_ring_pass.argtypes = [vp, vp, i64, i32, vp]
+    lib.cpattn_ring_prefill_overlapped.argtypes = [ctypes.POINTER(_PrefillDesc), i32, vp, ctypes.POINTER(vp),
+                                                   ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
+                                                   ctypes.POINTER(_Partial), i32, vp, vp]
     lib.cpattn_merge.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, ctypes.POINTER(_Partial),
                                  vp, vp, vp]
     lib.cpattn_passq_decode.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
@@ -257,6 +264,50 @@ def ring_step_partial(desc: PrefillDesc, rank: int, step: int, q_local, k_blk, v
                                         _stream(stream)), "cpattn_ring_step_partial")
 
 
+def ring_pass(src, dst, workgroups: int, stream=None) -> None:
+    """cpattn_ring_pass: device copy of src into dst (same byte size) on at most
+    `workgroups` workgroups, the emulated transfer of a KV block."""
+    lib = load()
+    for t in (src, dst):
+        if not t.is_cuda or not t.is_contiguous() or t.data_ptr() % 16:
+            raise ValueError("contiguous, 16-byte aligned device tensors expected")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst sizes differ")
+    _check(lib.cpattn_ring_pass(src.data_ptr(), dst.data_ptr(), nbytes, workgroups, _stream(stream)),
+           "cpattn_ring_pass")
+
+
+def ring_prefill_overlapped(desc: PrefillDesc, rank: int, q_local, k_blocks: Sequence, v_blocks: Sequence,
+                            k_recv: Sequence, v_recv: Sequence, acc: Partial, link_workgroups: int,
+                            compute_stream=None, transfer_stream=None) -> None:
+    """cpattn_ring_prefill_overlapped (see include/cpattn.h): the cp ring steps of
+    `rank` on compute_stream, the block transfers into the receive buffers
+    k_recv / v_recv (two or more each) on transfer_stream."""
+    lib = load()
+    rows = int(np.asarray(desc.cu_seqlens)[-1]) // desc.cp
+    if len(k_blocks) != desc.cp or len(v_blocks) != desc.cp:
+        raise ValueError("need cp K and V blocks")
+    if len(k_recv) != len(v_recv) or len(k_recv) < 2:
+        raise ValueError("need as many K as V receive buffers, at least two")
+    _dev_check(q_local, desc.dtype)
+    if tuple(q_local.shape) != (rows, desc.n_hq, desc.head_dim):
+        raise ValueError("q_local shape mismatch")
+    for t in list(k_blocks) + list(v_blocks) + list(k_recv) + list(v_recv):
+        _dev_check(t, desc.dtype)
+        if tuple(t.shape) != (rows, desc.n_kv, desc.head_dim):
+            raise ValueError(f"block shape {tuple(t.shape)} != {(rows, desc.n_kv, desc.head_dim)}")
+    if tuple(acc.num.shape) != (rows, desc.n_hq, desc.head_dim):
+        raise ValueError("acc shape mismatch")
+    d, keep = desc._c()
+    p = acc._c()
+    arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    _check(lib.cpattn_ring_prefill_overlapped(ctypes.byref(d), rank, q_local.data_ptr(), arr(k_blocks),
+                                              arr(v_blocks), arr(k_recv), arr(v_recv), len(k_recv), ctypes.byref(p),
+                                              link_workgroups, _stream(compute_stream),
+                                              _stream(transfer_stream)), "cpattn_ring_prefill_overlapped")
+
+
 def merge(acc: Partial, parts: Sequence[Partial] = (), out=None, lse=None, stream=None) -> None:
     """cpattn_merge: acc = merge(acc, *parts); optionally out = num/den, lse = m + ln den."""
     lib = load()
@@ -326,3 +377,6 @@ def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, sh
 
 def version() -> str:
     return load().cpattn_version().decode()
+
+
+from . import overlap  # noqa: E402  (transfer/compute overlap harness built on the entry points above)

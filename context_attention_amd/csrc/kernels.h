@@ -77,4 +77,9 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float &m, floa
   a2 = (m2 == kNegInf) ? 0.f : expf(m2 - m);
 }
 
+// Validation of a prefill description and (rank, step) shared by the ring-step
+// entry points (CPATTN_OK or the error code; no device call).
+__attribute__((visibility("hidden"))) int check_prefill(const cpattn_prefill_desc *desc, int32_t rank,
+                                                          int32_t step);
+
 }  // namespace cpattn

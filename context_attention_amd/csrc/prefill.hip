@@ -997,17 +997,13 @@ hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int un
 }  // namespace
 }  // namespace cpattn
 
-extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
-                                        const void *q_local, const void *k_blk, const void *v_blk,
-                                        const cpattn_partial *dst, int32_t accumulate, hipStream_t stream) {
-  using namespace cpattn;
-  if (desc == nullptr || dst == nullptr) return CPATTN_E_ARG;
+int cpattn::check_prefill(const cpattn_prefill_desc *desc, int32_t rank, int32_t step) {
+  if (desc == nullptr) return CPATTN_E_ARG;
   const int cp = desc->cp;
   if (cp < 1 || rank < 0 || rank >= cp || step < 0 || step >= cp) return CPATTN_E_ARG;
   if (desc->num_seqs < 0 || (desc->num_seqs > 0 && desc->cu_seqlens == nullptr)) return CPATTN_E_ARG;
   if (desc->n_hq < 1 || desc->n_kv < 1) return CPATTN_E_ARG;
   if (desc->dtype != CPATTN_DT_F32 && desc->dtype != CPATTN_DT_BF16) return CPATTN_E_ARG;
-  if (accumulate != 0 && accumulate != 1) return CPATTN_E_ARG;
   if (!(desc->scale > 0.f) || !(desc->scale < __builtin_huge_valf())) return CPATTN_E_ARG;
   if (desc->n_hq % desc->n_kv != 0) return CPATTN_E_DIVISIBILITY;
   const int d = desc->head_dim;
@@ -1021,6 +1017,20 @@ extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t
     if (L % (2 * (int64_t)cp) != 0) return CPATTN_E_DIVISIBILITY;
     if (L / (2 * cp) > (int64_t)1 << 30) return CPATTN_E_UNSUPPORTED;
   }
+  return CPATTN_OK;
+}
+
+extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
+                                        const void *q_local, const void *k_blk, const void *v_blk,
+                                        const cpattn_partial *dst, int32_t accumulate, hipStream_t stream) {
+  using namespace cpattn;
+  if (desc == nullptr || dst == nullptr) return CPATTN_E_ARG;
+  const int chk = check_prefill(desc, rank, step);
+  if (chk != CPATTN_OK) return chk;
+  if (accumulate != 0 && accumulate != 1) return CPATTN_E_ARG;
+  const int cp = desc->cp;
+  const int d = desc->head_dim;
+  const int64_t *cu = desc->cu_seqlens;
   const int64_t total = desc->num_seqs > 0 ? cu[desc->num_seqs] : 0;
   if (total == 0) return CPATTN_OK;
   if (q_local == nullptr || k_blk == nullptr || v_blk == nullptr || dst->m == nullptr || dst->den == nullptr ||

@@ -1,0 +1,131 @@
+"""One-GPU emulation of the pass-KV ring's transfer/compute overlap.
+
+The G5 context-parallel modelling spec fixes the ring's dependency contract
+(Rationale: step i's transfer runs concurrently with step i's compute; step
+i+1's compute waits for step i's transfer) and two acceptance checks
+(Acceptance table): "overlap effective" -- with a compute/transfer time ratio
+in [0.5, 2], the ring takes at most 1.1 x max(compute, transfer) and at most
+0.7 x (compute + transfer), which a serial ring (ratio 1.0 to the sum) fails
+-- and "overlap metamorphic" -- with a large S/cp, the ring deviates from the
+pure compute time by less than 10%.
+
+Here compute = the cp ring steps of one rank run back to back on one stream,
+transfer = its cp-1 block transfers (cpattn_ring_pass, K and V) back to back
+on one stream, ring = cpattn_ring_prefill_overlapped on two streams (three
+receive buffers by default), serial = the same call with one stream for both.
+`workgroups` = 0 runs the transfers on a DMA copy engine. Times are medians of
+HIP-event intervals on the stream the work ends on. Only the library's entry
+points run on the GPU; torch supplies memory, streams and events.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Sequence
+
+import numpy as np
+
+from . import (Partial, PrefillDesc, new_partial, ring_pass, ring_prefill_overlapped,
+               ring_step_partial)
+
+LOW, HIGH = 0.5, 2.0          # the middle band of compute/transfer ratios
+MAX_FACTOR, SUM_FACTOR = 1.1, 0.7
+METAMORPHIC_LIMIT = 0.10
+
+
+@dataclass
+class RingInputs:
+    desc: PrefillDesc
+    rank: int
+    q: "torch.Tensor"
+    k_blocks: List["torch.Tensor"]     # block held by each rank, [S/cp, n_kv, d]
+    v_blocks: List["torch.Tensor"]
+    k_recv: List["torch.Tensor"]       # n_recv receive buffers each
+    v_recv: List["torch.Tensor"]
+    acc: Partial
+
+    @property
+    def block_bytes(self) -> int:
+        t = self.k_blocks[0]
+        return t.numel() * t.element_size()
+
+
+def make_inputs(desc: PrefillDesc, rank: int, q, k_blocks: Sequence, v_blocks: Sequence,
+                n_recv: int = 3) -> RingInputs:
+    import torch
+    rows = int(np.asarray(desc.cu_seqlens)[-1]) // desc.cp
+    recv = lambda: [torch.empty_like(k_blocks[0]) for _ in range(n_recv)]
+    return RingInputs(desc, rank, q, list(k_blocks), list(v_blocks), recv(), recv(),
+                      new_partial(rows, desc.n_hq, desc.head_dim, device=q.device))
+
+
+def _median_ms(fn, stream, reps: int, warmup: int) -> float:
+    import torch
+    times = []
+    for i in range(warmup + reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def compute_ms(x: RingInputs, stream, reps: int = 5, warmup: int = 1) -> float:
+    cp = x.desc.cp
+
+    def run():
+        for i in range(cp):
+            j = (x.rank - i) % cp
+            ring_step_partial(x.desc, x.rank, i, x.q, x.k_blocks[j], x.v_blocks[j], x.acc,
+                              accumulate=i > 0, stream=stream)
+    return _median_ms(run, stream, reps, warmup)
+
+
+def transfer_ms(x: RingInputs, workgroups: int, stream, reps: int = 5, warmup: int = 1) -> float:
+    cp = x.desc.cp
+
+    def run():
+        for i in range(cp - 1):
+            src = (x.rank - i - 1) % cp
+            ring_pass(x.k_blocks[src], x.k_recv[i % len(x.k_recv)], workgroups, stream)
+            ring_pass(x.v_blocks[src], x.v_recv[i % len(x.v_recv)], workgroups, stream)
+    return _median_ms(run, stream, reps, warmup)
+
+
+def ring_ms(x: RingInputs, workgroups: int, compute_stream, transfer_stream, reps: int = 5,
+            warmup: int = 1) -> float:
+    def run():
+        ring_prefill_overlapped(x.desc, x.rank, x.q, x.k_blocks, x.v_blocks, x.k_recv, x.v_recv, x.acc,
+                                workgroups, compute_stream, transfer_stream)
+    return _median_ms(run, compute_stream, reps, warmup)
+
+
+def overlap_effective(x: RingInputs, workgroups: int, compute_stream, transfer_stream, reps: int = 5) -> dict:
+    """The spec's "overlap effective" measurement at one transfer width."""
+    t_c = compute_ms(x, compute_stream, reps)
+    t_t = transfer_ms(x, workgroups, compute_stream, reps)
+    t_r = ring_ms(x, workgroups, compute_stream, transfer_stream, reps)
+    t_s = ring_ms(x, workgroups, compute_stream, compute_stream, reps)
+    big, total = max(t_c, t_t), t_c + t_t
+    return {
+        "workgroups": workgroups, "compute_ms": t_c, "transfer_ms": t_t, "ring_ms": t_r, "serial_ms": t_s,
+        "ratio": t_t / t_c, "in_band": LOW <= t_t / t_c <= HIGH,
+        "ring_over_max": t_r / big, "ring_over_sum": t_r / total, "serial_over_sum": t_s / total,
+        "overlap_effective": t_r <= MAX_FACTOR * big and t_r <= SUM_FACTOR * total,
+        "serial_rejected": not (t_s <= MAX_FACTOR * big and t_s <= SUM_FACTOR * total),
+        "transfer_gb_per_s": 2 * (x.desc.cp - 1) * x.block_bytes / (t_t * 1e6),
+    }
+
+
+def overlap_metamorphic(x: RingInputs, workgroups: int, compute_stream, transfer_stream, reps: int = 3) -> dict:
+    """The spec's "overlap metamorphic" check: at large S/cp the overlapped ring
+    stays within 10% of the pure compute time."""
+    t_c = compute_ms(x, compute_stream, reps)
+    t_t = transfer_ms(x, workgroups, compute_stream, reps)
+    t_r = ring_ms(x, workgroups, compute_stream, transfer_stream, reps)
+    dev = abs(t_r - t_c) / t_c
+    return {"workgroups": workgroups, "compute_ms": t_c, "transfer_ms": t_t, "ring_ms": t_r,
+            "deviation": dev, "within_limit": dev < METAMORPHIC_LIMIT}

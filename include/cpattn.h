@@ -131,6 +131,54 @@ int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int3
                              const void *q_local, const void *k_blk, const void *v_blk,
                              const cpattn_partial *dst, int32_t accumulate, hipStream_t stream);
 
+/* Emulated pass-KV transfer (Definitions table, "Pass-KV": each ring step a
+ * rank forwards the KV block in hand to its successor). On one GPU the
+ * point-to-point transfer is a device copy of `bytes` from src to dst:
+ *   workgroups = 0      on a DMA (SDMA) copy engine, using no compute unit, as
+ *                       a transfer over xGMI does; runs beside any kernel.
+ *   workgroups 1..65535 by a copy kernel of at most that many 256-thread
+ *                       workgroups (about one link's worth of bandwidth for a
+ *                       few workgroups); it only runs beside another stream's
+ *                       kernel while that kernel leaves compute units free.
+ *   src, dst    device, 16-byte aligned, non-overlapping; bytes % 16 == 0, >= 0.
+ * Errors: E_ARG, E_DEVICE. */
+int cpattn_ring_pass(const void *src, void *dst, int64_t bytes, int32_t workgroups, hipStream_t stream);
+
+/* The whole pass-KV ring of one rank with transfers overlapping compute
+ * (Rationale: the ring's dependency contract; Acceptance, "overlap
+ * effective"). For step i = 0 .. cp-1 it enqueues on `compute` the ring step
+ * of cpattn_ring_step_partial (step 0 writes acc, later steps merge into it)
+ * on the block in hand, and for i < cp-1 on `transfer` the cpattn_ring_pass
+ * copies (K and V) that deliver the block of rank (rank - i - 1) mod cp for
+ * step i+1 into receive buffer i % n_recv. Events carry exactly these edges:
+ * compute(i) waits for transfer(i-1); transfer(i) follows transfer(i-1) and,
+ * when i+1-n_recv >= 1, waits for compute(i+1-n_recv), which read the buffer
+ * it overwrites (more buffers give a transfer more slack).
+ * No edge runs from compute(i) to transfer(i): the two run concurrently.
+ * When the call returns, all enqueued work is ordered before later work on
+ * `compute` (compute(cp-1) waits for the last transfer).
+ *   desc, rank, q_local  as for cpattn_ring_step_partial.
+ *   k_blocks, v_blocks   HOST arrays of cp device pointers: the block each rank
+ *                        holds ([S/cp, n_kv, head_dim], that rank's local
+ *                        order); entry j stands for rank j's memory, read by
+ *                        the transfers and, for j = rank, by step 0.
+ *   k_recv, v_recv       HOST arrays of n_recv device pointers each: the receive
+ *                        buffers, one block each, pairwise disjoint and disjoint
+ *                        from the blocks (unused when cp = 1).
+ *   n_recv               2 .. 16 when cp > 1.
+ *   acc                  device triple for S/cp rows (written, then merged into).
+ *   link_workgroups      `workgroups` of each transfer (0: copy engine), as for
+ *                        cpattn_ring_pass.
+ *   compute, transfer    streams; passing the same stream serialises the ring.
+ * Errors: those of cpattn_ring_step_partial and cpattn_ring_pass, returned
+ * before any work is enqueued; E_DEVICE if the runtime refuses an event or a
+ * launch part-way. */
+int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, int32_t rank, const void *q_local,
+                                   const void *const *k_blocks, const void *const *v_blocks,
+                                   void *const *k_recv, void *const *v_recv, int32_t n_recv,
+                                   const cpattn_partial *acc, int32_t link_workgroups, hipStream_t compute,
+                                   hipStream_t transfer);
+
 /* Merge and finalize (Definitions table, "Partial attention": the merge is
  * associative and order-independent).
  *   acc   in/out device triple [rows, n_hq(, head_dim)]: acc = merge(acc, parts[0], ...,

@@ -167,3 +167,54 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
                          scale=0.1)
     assert lib.cpattn_passq_decode(ctypes.byref(bad), None, None, None, None, None, None, None,
                                    ctypes.byref(n), None) == ca.E_UNSUPPORTED
+
+
+def test_ring_transfer_entry_points_reject_bad_arguments_without_gpu():
+    """cpattn_ring_pass and cpattn_ring_prefill_overlapped validate everything
+    before any device call (no event, no launch), so the error paths run on
+    the CPU."""
+    lib = ca.load()
+    vp = ctypes.c_void_p
+    # ring_pass: size, alignment, workgroups, overlap
+    assert lib.cpattn_ring_pass(vp(4096), vp(8192), 0, 1, None) == ca.OK          # nothing to copy
+    assert lib.cpattn_ring_pass(vp(4096), vp(1 << 20), -16, 1, None) == ca.E_ARG
+    assert lib.cpattn_ring_pass(vp(4096), vp(1 << 20), 24, 1, None) == ca.E_ARG     # not a multiple of 16
+    assert lib.cpattn_ring_pass(vp(4100), vp(1 << 20), 32, 1, None) == ca.E_ARG     # misaligned
+    assert lib.cpattn_ring_pass(vp(4096), vp(1 << 20), 32, -1, None) == ca.E_ARG    # negative width
+    assert lib.cpattn_ring_pass(vp(4096), vp(1 << 20), 32, 65536, None) == ca.E_ARG
+    assert lib.cpattn_ring_pass(vp(4096), vp(4096 + 16), 64, 1, None) == ca.E_ARG   # overlapping ranges
+    assert lib.cpattn_ring_pass(None, vp(4096), 64, 1, None) == ca.E_ARG
+
+    cu = np.array([0, 64], dtype=np.int64)
+    P = ctypes.POINTER(ctypes.c_int64)
+    d = ca._PrefillDesc(cp=2, num_seqs=1, cu_seqlens=cu.ctypes.data_as(P), n_hq=4, n_kv=2, head_dim=128,
+                        dtype=ca.DT_BF16, scale=0.125)
+    block = 32 * 2 * 128 * 2            # S/cp rows x n_kv x head_dim x 2 bytes
+    base = 1 << 24
+    kb = (vp * 2)(base, base + block)
+    vb = (vp * 2)(base + 2 * block, base + 3 * block)
+    kr = (vp * 2)(base + 4 * block, base + 5 * block)
+    vr = (vp * 2)(base + 6 * block, base + 7 * block)
+    n_recv = 2
+    part = ca._Partial(16, 16, 16)
+    q = vp(base + 8 * block)
+
+    def call(desc=d, rank=0, k=kb, v=vb, krx=kr, vrx=vr, nr=n_recv, wg=4):
+        return lib.cpattn_ring_prefill_overlapped(ctypes.byref(desc), rank, q, k, v, krx, vrx, nr,
+                                                  ctypes.byref(part), wg, None, None)
+    assert call(rank=2) == ca.E_ARG
+    assert call(wg=-1) == ca.E_ARG
+    assert call(krx=None) == ca.E_ARG
+    assert call(nr=1) == ca.E_ARG
+    assert call(nr=17) == ca.E_ARG
+    bad = ca._PrefillDesc(cp=2, num_seqs=1, cu_seqlens=cu.ctypes.data_as(P), n_hq=4, n_kv=3, head_dim=128,
+                          dtype=ca.DT_BF16, scale=0.125)
+    assert call(desc=bad) == ca.E_DIVISIBILITY
+    bad = ca._PrefillDesc(cp=2, num_seqs=1, cu_seqlens=cu.ctypes.data_as(P), n_hq=4, n_kv=2, head_dim=96,
+                          dtype=ca.DT_BF16, scale=0.125)
+    assert call(desc=bad) == ca.E_UNSUPPORTED
+    # a receive buffer overlapping a source block, or another receive buffer
+    assert call(krx=(vp * 2)(base + block // 2, base + 5 * block)) == ca.E_ARG
+    assert call(vrx=(vp * 2)(base + 4 * block + 16, base + 7 * block)) == ca.E_ARG
+    # misaligned block
+    assert call(k=(vp * 2)(base + 8, base + block)) == ca.E_ARG
