@@ -85,9 +85,9 @@ struct Cfg<128> {
 };
 template <>
 struct Cfg<512> {
-  static constexpr int BN = 32, NW = 4, NB = 1, WPE = 1;
+  static constexpr int BN = 32, NW = 8, NB = 1, WPE = 2;
+  static constexpr int NS = 4;   // waves that share a 32-row block, each owning D / NS columns
 };
-constexpr int kWideHalf = 256;   // head_dim 512: each wave of a pair owns half of d
 template <int D>
 constexpr int kThreadsOf = 64 * Cfg<D>::NW;
 // Rescale threshold of the running max in the exp2 domain: the numerator and
@@ -543,13 +543,15 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 // ----------------------------------------------------------------------------
 // head_dim 512 (bf16): wave pairs split d.
 // ----------------------------------------------------------------------------
-// A workgroup of 4 waves (one per SIMD) is two pairs; the two waves of a pair own
-// the same 32 query rows and one half of d each: Q and the output accumulator of
-// a wave cover its 256 columns (64 + 128 registers). QK^T is split over d too:
-// each wave multiplies its half, the pair exchanges the two partial 32 x 32 score
-// tiles through LDS and both add them, so both hold the full scores and run the
-// same softmax; the PV product then fills each wave's half of the output. Keys
-// come in 32-key tiles copied straight into double-buffered LDS.
+// A workgroup of 8 waves (two per SIMD) is two groups of NS = 4; the waves of a
+// group own the same 32 query rows and a quarter of d each: Q and the output
+// accumulator of a wave cover its 128 columns (32 + 64 registers), which keeps
+// a wave within the 256 registers of two waves per SIMD. QK^T is split over d
+// too: each wave multiplies its quarter, the group exchanges the partial 32 x 32
+// score tiles through LDS and every wave adds the four in the same order, so all
+// hold bit-identical scores and run the same softmax; the PV product then fills
+// each wave's quarter of the output. Keys come in 32-key tiles copied straight
+// into double-buffered LDS (2 x 32 KB for K and for V, 32 KB of partial scores).
 __device__ __forceinline__ void put_scores(f32x4_t (*x)[64], const f32x16_t &s) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -571,14 +573,16 @@ __device__ __forceinline__ f32x16_t get_scores(const f32x4_t (*x)[64]) {
 }
 
 template <int HG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreadsOf<512>) __attribute__((amdgpu_waves_per_eu(Cfg<512>::WPE, Cfg<512>::WPE)))
 void ring_step_wide(SeqTable tab, StepArgs a) {
   constexpr int D = 512;
   constexpr int BN = Cfg<D>::BN;                // 32 keys per tile
-  constexpr int NP = Cfg<D>::NW / 2;            // pairs per workgroup
-  constexpr int BM = 32 * NP / HG;              // query rows per workgroup
-  constexpr int KSH = kWideHalf / 16;           // QK^T k-steps over one half of d
-  constexpr int DBH = kWideHalf / 32;           // output d blocks of one half
+  constexpr int NS = Cfg<D>::NS;                // waves per row block
+  constexpr int NG = Cfg<D>::NW / NS;           // row blocks (groups) per workgroup
+  constexpr int BM = 32 * NG / HG;              // query rows per workgroup
+  constexpr int DW = D / NS;                    // columns of d per wave
+  constexpr int KSH = DW / 16;                  // QK^T k-steps over a wave's columns
+  constexpr int DBH = DW / 32;                  // output d blocks of a wave
   constexpr int KSZ = BN * D;
   constexpr int VSZ = BN * D;
 
@@ -593,7 +597,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int lane = tid & 63;
   const int qi = lane & 31;
   const int hf = lane >> 5;
-  const int pair = wave >> 1, dh = wave & 1;
+  const int grp = wave / NS, dh = wave % NS;
 
   const int n_hg = a.n_hq / HG;
   int unit, hg;
@@ -607,10 +611,10 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int qa = tail ? a.a_tail : a.a_head;
   const int64_t qrow0 = tab.row_off[si] + (tail ? c : 0);
 
-  const int h = hg * HG + (pair % HG);
+  const int h = hg * HG + (grp % HG);
   const int rep = a.n_hq / a.n_kv;
   const int g = h / rep;
-  const int wrow0 = tile * BM + (pair / HG) * 32;
+  const int wrow0 = tile * BM + (grp / HG) * 32;
   const int wg_row_end = min(c, tile * BM + BM);
 
   const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
@@ -629,7 +633,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int64_t grow = qrow0 + row;
   float *mptr = a.m + (grow * a.n_hq + h);
   float *dptr = a.den + (grow * a.n_hq + h);
-  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D + dh * kWideHalf;
+  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D + dh * DW;
 
   if (nseg == 0) {
     if (!a.accumulate && row_ok) {
@@ -647,7 +651,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   // Q fragments of this wave's half of d
   bf16x8_t qf[KSH];
   {
-    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + (grow * a.n_hq + h) * (int64_t)D + dh * kWideHalf + 8 * hf;
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + (grow * a.n_hq + h) * (int64_t)D + dh * DW + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSH; ++ks)
       qf[ks] = row_ok ? *reinterpret_cast<const bf16x8_t *>(qp + ks * 16)
@@ -714,8 +718,10 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     load_tile<D>(smap.k, tile_at(kblock, it + 2), Ks[cur]);
     load_tile<D>(smap.v, tile_at(vblock, it + 1), Vt[cur ^ 1]);
 
-    // full scores of tile it = own partial + the partner's partial
-    f32x16_t sacc = spart + get_scores(Sx[wave ^ 1]);
+    // full scores of tile it: the group's partials summed in one fixed order
+    f32x16_t sacc = get_scores(Sx[grp * NS]);
+#pragma unroll
+    for (int w = 1; w < NS; ++w) sacc += get_scores(Sx[grp * NS + w]);
     __syncthreads();   // both partials read before either is overwritten
 
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
@@ -759,7 +765,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int db = 0; db < DBH; ++db) {
-        const int d0 = dh * kWideHalf + db * 32;
+        const int d0 = dh * DW + db * 32;
         const bf16x8_t vf = v_fragment<D>(Vc, ks, d0);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
@@ -771,7 +777,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  // both waves of a pair read the old max and denominator; every wave reaches the
+  // all waves of a group read the old max and denominator; every wave reaches the
   // barrier before one of them overwrites them
   float m_old = kNegInf, d_old = 0.f;
   if (a.accumulate && row_ok) {
@@ -944,7 +950,7 @@ template <int HG>
 hipError_t launch_wide(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
   const int n_hg = a.n_hq / HG;
   const int64_t blocks = (int64_t)units * n_hg;
-  hipLaunchKernelGGL((ring_step_wide<HG>), dim3((unsigned)blocks), dim3(256), 0, s, t, a);
+  hipLaunchKernelGGL((ring_step_wide<HG>), dim3((unsigned)blocks), dim3(kThreadsOf<512>), 0, s, t, a);
   return hipGetLastError();
 }
 
@@ -979,7 +985,7 @@ bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || 
 
 int rows_per_unit(int dtype, int d, int rep) {
   if (!use_mfma(dtype, d)) return 1;
-  if (d == 512) return 32 * (Cfg<512>::NW / 2) / pick_hg_d(512, rep);
+  if (d == 512) return 32 * (Cfg<512>::NW / Cfg<512>::NS) / pick_hg_d(512, rep);
   return 32 * Cfg<128>::NB * Cfg<128>::NW / pick_hg(rep);
 }
 
