@@ -94,14 +94,10 @@ def overlap_report(ca, synth, torch, pdesc, q0, blocks):
     ring steps (cpattn_ring_prefill_overlapped, three receive buffers), after
     the timed steps: the headline rank-0 share (the spec's large-S/cp
     metamorphic check, < 10% from pure compute) and a middle-band ring (MHA,
-    64 heads, S=16384, cp=8, rank 3; transfer/compute ratio in [0.5, 2])."""
+    64 heads, S=16384, cp=8, rank 3; transfer/compute ratio in [0.5, 2]). Both
+    run on the dedicated stream pair that a probe of the middle-band ring finds
+    fastest (overlap.stream_pair); the probe's spread is reported."""
     ov = ca.overlap
-    comp, xfer = torch.cuda.Stream(), torch.cuda.Stream()
-    log("bench: overlap, headline share")
-    x = ov.make_inputs(pdesc, 0, q0, [k for k, _ in blocks], [v for _, v in blocks], n_recv=3)
-    meta = ov.overlap_metamorphic(x, 0, comp, xfer, reps=1)
-    del x
-    log("bench: overlap, middle band")
     w = synth.PrefillWorkload(name="mha 16384", seqlens=[16384], cp=8, n_hq=64, n_kv=64, head_dim=128,
                               dtype="bf16", scale_in=0.5, seed=1)
     S = w.total_tokens
@@ -117,9 +113,20 @@ def overlap_report(ca, synth, torch, pdesc, q0, blocks):
     del full
     desc = ca.PrefillDesc(cp=w.cp, cu_seqlens=w.cu_seqlens, n_hq=w.n_hq, n_kv=w.n_kv, head_dim=w.head_dim,
                           dtype=w.dtype, scale=w.softmax_scale)
-    band = ov.overlap_effective(ov.make_inputs(desc, 3, q3, kb, vb, n_recv=3), 0, comp, xfer, reps=5)
+    xb = ov.make_inputs(desc, 3, q3, kb, vb, n_recv=3)
+    log("bench: overlap, choosing the stream pair")
+    comp, xfer, probes = ov.stream_pair(xb, 0)
+    log("bench: overlap, headline share")
+    x = ov.make_inputs(pdesc, 0, q0, [k for k, _ in blocks], [v for _, v in blocks], n_recv=3)
+    meta = ov.overlap_metamorphic(x, 0, comp, xfer, reps=1)
+    del x
+    log("bench: overlap, middle band")
+    band = ov.overlap_effective(xb, 0, comp, xfer, reps=5)
     rnd = lambda d: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items() if k != "workgroups"}
+    pt = sorted(probes.values())
     return {"transfer": "DMA copy engine", "receive_buffers": 3,
+            "stream_pair_probe_ms": {"best": round(pt[0], 4), "median": round(pt[len(pt) // 2], 4),
+                                     "worst": round(pt[-1], 4), "pairs": len(pt)},
             "headline_share": rnd(meta),
             "middle_band": dict(workload="MHA 64 heads, d128, S=16384, cp=8, rank 3", **rnd(band))}
 

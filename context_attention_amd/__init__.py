@@ -6,7 +6,7 @@ streams. The binding fails loudly when the library has not been built; there
 is no fallback path.
 
 Entry points mirror the C names of include/cpattn.h:
-    balanced_split, ring_step_partial, ring_pass, ring_prefill_overlapped,
+    balanced_split, balanced_split_padded, ring_step_partial, ring_pass, ring_prefill_overlapped,
     merge, passq_decode, account
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
-    "balanced_split", "ring_step_partial", "ring_pass", "ring_prefill_overlapped", "merge",
+    "balanced_split", "balanced_split_padded", "ring_step_partial", "ring_pass", "ring_prefill_overlapped", "merge",
     "passq_decode", "passq_workspace_bytes",
     "account", "new_partial",
 ]
@@ -33,7 +33,7 @@ _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPP
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
 
-EXPORTS = ["cpattn_balanced_split", "cpattn_ring_step_partial", "cpattn_ring_pass",
+EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
            "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_passq_decode", "cpattn_account",
            "cpattn_version"]
 
@@ -54,7 +54,7 @@ class _PrefillDesc(ctypes.Structure):
     _fields_ = [("cp", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("cu_seqlens", ctypes.POINTER(ctypes.c_int64)),
                 ("n_hq", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("padded", ctypes.c_int32)]
 
 
 class _DecodeDesc(ctypes.Structure):
@@ -97,6 +97,7 @@ def load():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.cpattn_balanced_split.argtypes = [ctypes.POINTER(ctypes.c_int64), i32, i32, i32,
                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.cpattn_balanced_split_padded.argtypes = lib.cpattn_balanced_split.argtypes
     lib.cpattn_ring_step_partial.argtypes = [ctypes.POINTER(_PrefillDesc), i32, i32, vp, vp, vp,
                                              ctypes.POINTER(_Partial), i32, vp]
     lib.cpattn_ring_pass.argtypes = [vp, vp, i64, i32, vp]
@@ -142,6 +143,26 @@ def balanced_split(cu_seqlens, cp: int, rank: int):
     _check(lib.cpattn_balanced_split(_i64_ptr(cu), n, cp, rank, _i64_ptr(pos), _i64_ptr(cul)),
            "cpattn_balanced_split")
     return pos[: total // cp], cul
+
+
+def balanced_split_padded(cu_seqlens, cp: int, rank: int):
+    """cpattn_balanced_split_padded: returns (positions int64 [sum(Lp)/cp] with -1
+    for pad rows, cu_local int64 [n+1])."""
+    lib = load()
+    cu = _i64_array(cu_seqlens)
+    n = cu.size - 1
+    rows = padded_rows(cu, cp)
+    pos = np.zeros(max(rows, 1), dtype=np.int64)
+    cul = np.zeros(n + 1, dtype=np.int64)
+    _check(lib.cpattn_balanced_split_padded(_i64_ptr(cu), n, cp, rank, _i64_ptr(pos), _i64_ptr(cul)),
+           "cpattn_balanced_split_padded")
+    return pos[:rows], cul
+
+
+def padded_rows(cu_seqlens, cp: int) -> int:
+    """Local rows of one rank when every sequence is padded to a multiple of 2*cp."""
+    L = np.diff(_i64_array(cu_seqlens))
+    return int(np.sum(2 * ((L + 2 * cp - 1) // (2 * cp))))
 
 
 def account(*, cp: int, n_hq: int, n_kv: int, head_dim: int, dtype_bytes: int, cu_seqlens=None,
@@ -191,12 +212,20 @@ class PrefillDesc:
     head_dim: int
     dtype: str       # 'bf16' or 'f32'
     scale: float
+    padded: bool = False   # sequences padded to a multiple of 2*cp (see include/cpattn.h)
+
+    @property
+    def rows(self) -> int:
+        """Rows of one rank's local buffers (pad rows included)."""
+        if self.padded:
+            return padded_rows(self.cu_seqlens, self.cp)
+        return int(np.asarray(self.cu_seqlens)[-1]) // self.cp
 
     def _c(self):
         cu = _i64_array(self.cu_seqlens)
         d = _PrefillDesc(cp=self.cp, num_seqs=cu.size - 1, cu_seqlens=_i64_ptr(cu), n_hq=self.n_hq,
                          n_kv=self.n_kv, head_dim=self.head_dim, dtype=_dtype_code(self.dtype),
-                         scale=self.scale)
+                         scale=self.scale, padded=int(bool(self.padded)))
         return d, cu
 
 
@@ -249,7 +278,7 @@ def ring_step_partial(desc: PrefillDesc, rank: int, step: int, q_local, k_blk, v
                       accumulate: bool = False, stream=None) -> None:
     """cpattn_ring_step_partial (see include/cpattn.h)."""
     lib = load()
-    rows = int(np.asarray(desc.cu_seqlens)[-1]) // desc.cp
+    rows = desc.rows
     for t, h in ((q_local, desc.n_hq), (k_blk, desc.n_kv), (v_blk, desc.n_kv)):
         _dev_check(t, desc.dtype)
         if tuple(t.shape) != (rows, h, desc.head_dim):
@@ -285,7 +314,7 @@ def ring_prefill_overlapped(desc: PrefillDesc, rank: int, q_local, k_blocks: Seq
     `rank` on compute_stream, the block transfers into the receive buffers
     k_recv / v_recv (two or more each) on transfer_stream."""
     lib = load()
-    rows = int(np.asarray(desc.cu_seqlens)[-1]) // desc.cp
+    rows = desc.rows
     if len(k_blocks) != desc.cp or len(v_blocks) != desc.cp:
         raise ValueError("need cp K and V blocks")
     if len(k_recv) != len(v_recv) or len(k_recv) < 2:

@@ -64,6 +64,29 @@ extern "C" int cpattn_balanced_split(const int64_t *cu_seqlens, int32_t num_seqs
   return CPATTN_OK;
 }
 
+extern "C" int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp,
+                                            int32_t rank, int64_t *positions, int64_t *cu_local) {
+  // the split of cpattn_balanced_split over sequences padded to a multiple of
+  // 2*cp; slots past the true length are pad rows (-1)
+  if (cp < 1 || rank < 0 || rank >= cp) return CPATTN_E_ARG;
+  if (positions == nullptr || cu_local == nullptr) return CPATTN_E_ARG;
+  const int rc = check_seqlens(cu_seqlens, num_seqs, 1);
+  if (rc != CPATTN_OK) return rc;
+  const int64_t two_cp = 2 * (int64_t)cp;
+  int64_t w = 0;
+  cu_local[0] = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t start = cu_seqlens[i];
+    const int64_t L = cu_seqlens[i + 1] - start;
+    const int64_t c = (L + two_cp - 1) / two_cp;
+    const int64_t chunks[2] = {(int64_t)rank * c, (two_cp - 1 - rank) * c};
+    for (const int64_t first : chunks)
+      for (int64_t x = 0; x < c; ++x) positions[w++] = (first + x < L) ? start + first + x : -1;
+    cu_local[i + 1] = cu_local[i] + 2 * c;
+  }
+  return CPATTN_OK;
+}
+
 extern "C" int cpattn_account(const cpattn_account_in *in, cpattn_account_out *out) {
   if (in == nullptr || out == nullptr) return CPATTN_E_ARG;
   const int64_t cp = in->cp;

@@ -31,7 +31,8 @@ constexpr int kMaxSeq = 64;  // sequences per launch (the host splits larger bat
 
 struct SeqTable {
   int32_t n;                      // sequences in this launch
-  int32_t c[kMaxSeq];             // chunk length c_i = L_i / (2 cp)
+  int32_t c[kMaxSeq];             // chunk length c_i = Lp_i / (2 cp), Lp_i = L_i rounded up to a multiple of 2 cp
+  int32_t len[kMaxSeq];           // true length L_i: slots at or past it are pad tokens
   int64_t row_off[kMaxSeq];       // first local row of sequence i (same in q and kv blocks)
   int32_t start[kMaxSeq + 1];     // prefix of work units (tiles or rows) per sequence
 };
@@ -50,6 +51,12 @@ struct StepArgs {
   float scale;             // softmax scale (natural units)
   int32_t accumulate;
 };
+
+// Real (non-pad) tokens of chunk `chunk` of a sequence of true length len
+// split into chunks of c slots.
+__device__ __forceinline__ int chunk_valid(int len, int chunk, int c) {
+  return max(0, min(c, len - chunk * c));
+}
 
 __device__ __forceinline__ int find_seq(const SeqTable &t, int32_t unit) {
   int i = 0;
@@ -167,12 +174,17 @@ template <int D>
 __device__ __forceinline__ void load_tile(const uint32_t (&off)[StageMap<D>::KN], u32x4_t rsrc, __bf16 *dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const int wave = threadIdx.x >> 6;
+  // the resource is uniform; readfirstlane keeps it in scalar registers
+  const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
+                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
+                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
 #pragma unroll
   for (int i = 0; i < StageMap<D>::KN; ++i) {
     __bf16 *chunk = dst + (wave * StageMap<D>::KN + i) * 512;   // 1 KB
     const uint32_t lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)chunk);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rsrc), "{m0}"(lds));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rs), "{m0}"(lds));
   }
 #endif
 }
@@ -251,13 +263,41 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[N
 // Tile geometry of flattened tile index t over the (up to two) key segments.
 template <int BN>
 struct Segs {
+  int nseg;               // non-empty segments (0, 1 or 2)
   int n0;                 // tiles of segment 0
   int64_t row[2];         // first key row of each segment in the block
   int end[2];             // visible keys of each segment
   bool diag[2];
   __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
   __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * BN; }
+  __device__ __forceinline__ int tiles() const {
+    return n0 + (nseg > 1 ? (end[1] + BN - 1) / BN : 0);
+  }
 };
+
+// The key segments of a workgroup whose query rows lie in chunk qa: the tail
+// key chunk, then the head key chunk, each kept when it is causally visible
+// and holds a real key. A diagonal segment (same chunk) ends at the
+// workgroup's last real row; others at the chunk's real keys.
+template <int BN>
+__device__ __forceinline__ Segs<BN> make_segs(const StepArgs &a, int qa, int c, int len, int64_t row_off,
+                                              int row_end) {
+  const bool diag_t = a.b_tail == qa, diag_h = a.b_head == qa;
+  const int end_t = min(diag_t ? row_end : c, chunk_valid(len, a.b_tail, c));
+  const int end_h = min(diag_h ? row_end : c, chunk_valid(len, a.b_head, c));
+  const bool ok_t = a.b_tail <= qa && end_t > 0;
+  const bool ok_h = a.b_head <= qa && end_h > 0;
+  Segs<BN> sg;
+  sg.nseg = (int)ok_t + (int)ok_h;
+  sg.row[0] = ok_t ? row_off + c : row_off;
+  sg.diag[0] = ok_t ? diag_t : diag_h;
+  sg.end[0] = ok_t ? end_t : (ok_h ? end_h : 0);
+  sg.row[1] = row_off;   // a second segment is always the head key chunk
+  sg.diag[1] = diag_h;
+  sg.end[1] = (ok_t && ok_h) ? end_h : 0;
+  sg.n0 = (sg.end[0] + BN - 1) / BN;
+  return sg;
+}
 
 template <int D, int HG>
 __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
@@ -303,25 +343,20 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   const int wg_row_end = min(c, tile * BM + BM);            // rows of the workgroup: [tile*BM, wg_row_end)
 
   // key segments that are not empty, the tail key chunk first
-  const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
-  const int nseg = (int)vis_t + (int)vis_h;
-  Segs<BN> sg;
-  sg.row[0] = vis_t ? tab.row_off[si] + c : tab.row_off[si];
-  sg.diag[0] = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
-  sg.end[0] = sg.diag[0] ? wg_row_end : c;
-  sg.row[1] = tab.row_off[si];
-  sg.diag[1] = a.b_head == qa;
-  sg.end[1] = sg.diag[1] ? wg_row_end : c;
-  sg.n0 = (sg.end[0] + BN - 1) / BN;
+  const int len = tab.len[si];
+  const int q_valid = chunk_valid(len, qa, c);              // real rows of this query chunk
+  const Segs<BN> sg = make_segs<BN>(a, qa, c, len, tab.row_off[si], min(wg_row_end, q_valid));
+  const int nseg = sg.nseg;
 
   int row[NB];
-  bool row_ok[NB];
+  bool row_ok[NB], row_in[NB];
   int64_t grow[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     row[nb] = wrow0 + nb * 32 + qi;
-    row_ok[nb] = row[nb] < c;
-    grow[nb] = qrow0 + row[nb];   // local row index in the rank's buffer
+    row_in[nb] = row[nb] < c;        // a row of the local buffer
+    row_ok[nb] = row[nb] < q_valid;  // a real (non-pad) row
+    grow[nb] = qrow0 + row[nb];      // local row index in the rank's buffer
   }
 
   if (nseg == 0) {
@@ -329,7 +364,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     if (!a.accumulate) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if (!row_ok[nb]) continue;
+        if (!row_in[nb]) continue;
         if (hf == 0) store_stats(a.m + grow[nb] * a.n_hq + h, a.den + grow[nb] * a.n_hq + h, kNegInf, 0.f);
         float *nptr = a.num + (grow[nb] * a.n_hq + h) * (int64_t)D;
 #pragma unroll
@@ -341,7 +376,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     }
     return;
   }
-  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + BN - 1) / BN : 0);
+  const int ntiles = sg.tiles();
 
   // Q fragments: B operands of S^T = K Q^T, lane holds q[row][ks*16 + 8*hf .. +8]
   const __bf16 *qbase = reinterpret_cast<const __bf16 *>(a.q);
@@ -508,12 +543,14 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   // ---- epilogue: natural-log max, full denominator, optional merge, store
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float l_tot = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    if (!row_ok[nb]) continue;
+    // a pad row is stored as a row that saw no key (the merge identity)
+    const float l_sum = l_run[nb] + __shfl_xor(l_run[nb], 32);
+    const float l_tot = row_ok[nb] ? l_sum : 0.f;
+    if (!row_in[nb]) continue;
     float *mptr = a.m + (grow[nb] * a.n_hq + h);
     float *dptr = a.den + (grow[nb] * a.n_hq + h);
     float *nptr = a.num + (grow[nb] * a.n_hq + h) * (int64_t)D;
-    const float m_nat = (m_ref[nb] == kNegInf) ? kNegInf : m_ref[nb] * a.scale;
+    const float m_nat = (m_ref[nb] == kNegInf || !row_ok[nb]) ? kNegInf : m_ref[nb] * a.scale;
     float w_old = 0.f, w_new = 1.f, m_out = m_nat;
     if (a.accumulate) {
       const float m_old = *mptr;
@@ -531,6 +568,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
         float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
         f32x4_t o = {oacc[nb][db][4 * g4], oacc[nb][db][4 * g4 + 1], oacc[nb][db][4 * g4 + 2],
                      oacc[nb][db][4 * g4 + 3]};
+        if (!row_ok[nb]) o = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (a.accumulate) {
           const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
           o = old * w_old + o * w_new;
@@ -617,26 +655,21 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int wrow0 = tile * BM + (grp / HG) * 32;
   const int wg_row_end = min(c, tile * BM + BM);
 
-  const bool vis_t = a.b_tail <= qa, vis_h = a.b_head <= qa;
-  const int nseg = (int)vis_t + (int)vis_h;
-  Segs<BN> sg;
-  sg.row[0] = vis_t ? tab.row_off[si] + c : tab.row_off[si];
-  sg.diag[0] = vis_t ? (a.b_tail == qa) : (a.b_head == qa);
-  sg.end[0] = sg.diag[0] ? wg_row_end : c;
-  sg.row[1] = tab.row_off[si];
-  sg.diag[1] = a.b_head == qa;
-  sg.end[1] = sg.diag[1] ? wg_row_end : c;
-  sg.n0 = (sg.end[0] + BN - 1) / BN;
+  const int len = tab.len[si];
+  const int q_valid = chunk_valid(len, qa, c);
+  const Segs<BN> sg = make_segs<BN>(a, qa, c, len, tab.row_off[si], min(wg_row_end, q_valid));
+  const int nseg = sg.nseg;
 
   const int row = wrow0 + qi;
-  const bool row_ok = row < c;
+  const bool row_in = row < c;          // a row of the local buffer
+  const bool row_ok = row < q_valid;    // a real (non-pad) row
   const int64_t grow = qrow0 + row;
   float *mptr = a.m + (grow * a.n_hq + h);
   float *dptr = a.den + (grow * a.n_hq + h);
   float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D + dh * DW;
 
   if (nseg == 0) {
-    if (!a.accumulate && row_ok) {
+    if (!a.accumulate && row_in) {
       if (hf == 0 && dh == 0) store_stats(mptr, dptr, kNegInf, 0.f);
 #pragma unroll
       for (int db = 0; db < DBH; ++db)
@@ -646,7 +679,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     }
     return;
   }
-  const int ntiles = sg.n0 + (nseg > 1 ? (sg.end[1] + BN - 1) / BN : 0);
+  const int ntiles = sg.tiles();
 
   // Q fragments of this wave's half of d
   bf16x8_t qf[KSH];
@@ -776,17 +809,19 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // a pad row is stored as a row that saw no key (the merge identity)
+  const float l_sum = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = row_ok ? l_sum : 0.f;
   // all waves of a group read the old max and denominator; every wave reaches the
   // barrier before one of them overwrites them
   float m_old = kNegInf, d_old = 0.f;
-  if (a.accumulate && row_ok) {
+  if (a.accumulate && row_in) {
     m_old = *mptr;
     d_old = *dptr;
   }
   __syncthreads();
-  if (!row_ok) return;
-  const float m_nat = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
+  if (!row_in) return;
+  const float m_nat = (m_ref == kNegInf || !row_ok) ? kNegInf : m_ref * a.scale;
   float w_old = 0.f, w_new = 1.f, m_out = m_nat;
   if (a.accumulate) {
     merge_weights(m_old, m_nat, m_out, w_old, w_new);
@@ -801,6 +836,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     for (int g4 = 0; g4 < 4; ++g4) {
       float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
       f32x4_t o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+      if (!row_ok) o = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if (a.accumulate) {
         const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
         o = old * w_old + o * w_new;
@@ -856,9 +892,11 @@ __global__ __launch_bounds__(kGenThreads) void ring_step_generic(SeqTable tab, S
   const int64_t grow = tab.row_off[si] + lr;
   const int rep = a.n_hq / a.n_kv;
   const int g = h / rep;
+  const int len = tab.len[si];
+  const bool real = qrow < chunk_valid(len, qa, c);   // pad rows see no key
 
   const T *qp = reinterpret_cast<const T *>(a.q) + (grow * a.n_hq + h) * (int64_t)D;
-  for (int d = tid; d < D; d += kGenThreads) qs[d] = Elem<T>::load1(qp + d);
+  for (int d = tid; d < D; d += kGenThreads) qs[d] = real ? Elem<T>::load1(qp + d) : 0.f;
   __syncthreads();
 
   const T *kb = reinterpret_cast<const T *>(a.k);
@@ -872,8 +910,8 @@ __global__ __launch_bounds__(kGenThreads) void ring_step_generic(SeqTable tab, S
 
   for (int sg = 0; sg < 2; ++sg) {
     const int b = sg == 0 ? a.b_head : a.b_tail;
-    if (b > qa) continue;
-    const int kend = (b == qa) ? qrow + 1 : c;
+    if (b > qa || !real) continue;
+    const int kend = min((b == qa) ? qrow + 1 : c, chunk_valid(len, b, c));
     const int64_t krow0 = tab.row_off[si] + (sg == 0 ? 0 : c);
     for (int k0 = 0; k0 < kend; k0 += kGenThreads) {
       const int key = k0 + tid;
@@ -1015,15 +1053,24 @@ int cpattn::check_prefill(const cpattn_prefill_desc *desc, int32_t rank, int32_t
   const int d = desc->head_dim;
   if (d != 64 && d != 128 && d != 512) return CPATTN_E_UNSUPPORTED;
   if (desc->n_hq > 65535) return CPATTN_E_UNSUPPORTED;
+  if (desc->padded != 0 && desc->padded != 1) return CPATTN_E_ARG;
   const int64_t *cu = desc->cu_seqlens;
   if (desc->num_seqs > 0 && cu[0] != 0) return CPATTN_E_ARG;
   for (int i = 0; i < desc->num_seqs; ++i) {
     const int64_t L = cu[i + 1] - cu[i];
     if (L < 0) return CPATTN_E_ARG;
-    if (L % (2 * (int64_t)cp) != 0) return CPATTN_E_DIVISIBILITY;
-    if (L / (2 * cp) > (int64_t)1 << 30) return CPATTN_E_UNSUPPORTED;
+    if (!desc->padded && L % (2 * (int64_t)cp) != 0) return CPATTN_E_DIVISIBILITY;
+    if (L > (int64_t)1 << 30) return CPATTN_E_UNSUPPORTED;
   }
   return CPATTN_OK;
+}
+
+int64_t cpattn::local_rows(const cpattn_prefill_desc *desc) {
+  const int64_t two_cp = 2 * (int64_t)desc->cp;
+  int64_t rows = 0;
+  for (int i = 0; i < desc->num_seqs; ++i)
+    rows += 2 * ((desc->cu_seqlens[i + 1] - desc->cu_seqlens[i] + two_cp - 1) / two_cp);
+  return rows;
 }
 
 extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
@@ -1072,12 +1119,14 @@ extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t
     t.start[0] = 0;
     int64_t units = 0;
     while (i < desc->num_seqs && t.n < kMaxSeq) {
-      const int64_t c = (cu[i + 1] - cu[i]) / (2 * cp);
+      const int64_t L = cu[i + 1] - cu[i];
+      const int64_t c = (L + 2 * cp - 1) / (2 * cp);   // = L / (2 cp) unless padded
       const int64_t u = mfma ? 2 * ((c + rpu - 1) / rpu) : 2 * c;
       const int64_t blocks_after = (units + u) * (mfma ? desc->n_hq / pick_hg_d(d, rep) : 1);
       if (t.n > 0 && blocks_after > 0x7FFFFFFFLL) break;
       if (blocks_after > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
       t.c[t.n] = (int32_t)c;
+      t.len[t.n] = (int32_t)L;
       t.row_off[t.n] = row_off;
       units += u;
       t.start[t.n + 1] = (int32_t)units;

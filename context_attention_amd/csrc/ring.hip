@@ -109,7 +109,7 @@ extern "C" int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, i
   if (q_local == nullptr || acc->m == nullptr || acc->den == nullptr || acc->num == nullptr) return CPATTN_E_ARG;
   if (k_blocks[rank] == nullptr || v_blocks[rank] == nullptr) return CPATTN_E_ARG;
   const int64_t elem = desc->dtype == CPATTN_DT_BF16 ? 2 : 4;
-  const int64_t block_bytes = total / cp * desc->n_kv * desc->head_dim * elem;
+  const int64_t block_bytes = local_rows(desc) * desc->n_kv * desc->head_dim * elem;
   if (cp > 1) {
     // every receive buffer is aligned, disjoint from every source block and from
     // every other receive buffer

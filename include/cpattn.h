@@ -68,14 +68,21 @@ typedef struct {
  *   cp          CP degree, >= 1.
  *   num_seqs    number of packed sequences, >= 0.
  *   cu_seqlens  HOST array [num_seqs + 1]: cu_seqlens[0] = 0, non-decreasing;
- *               sequence i holds global packed tokens [cu[i], cu[i+1]). Every
- *               length must be divisible by 2*cp (Definitions table, "Balanced
- *               chunk split": 2*cp chunks per sequence).
+ *               sequence i holds global packed tokens [cu[i], cu[i+1]). With
+ *               padded = 0 every length must be divisible by 2*cp (Definitions
+ *               table, "Balanced chunk split": 2*cp chunks per sequence).
  *   n_hq, n_kv  query heads and key/value heads; q head h reads kv head
  *               h / (n_hq / n_kv).
  *   head_dim    64, 128 or 512.
  *   dtype       element type of Q, K, V.
- *   scale       softmax scale applied to q.k (e.g. 1/sqrt(head_dim)), > 0, finite. */
+ *   scale       softmax scale applied to q.k (e.g. 1/sqrt(head_dim)), > 0, finite.
+ *   padded      0: lengths divisible by 2*cp. 1: sequence i of length L_i is
+ *               padded at its end to Lp_i, the next multiple of 2*cp, and split
+ *               as a sequence of Lp_i tokens (cpattn_balanced_split_padded); the
+ *               pad tokens take no part: no query sees them as keys and their
+ *               own rows get the identity triple. Local buffers then hold
+ *               sum(Lp_i)/cp rows, pad rows included (their contents are not
+ *               read). */
 typedef struct {
   int32_t cp;
   int32_t num_seqs;
@@ -85,6 +92,7 @@ typedef struct {
   int32_t head_dim;
   int32_t dtype;
   float scale;
+  int32_t padded;
 } cpattn_prefill_desc;
 
 /* Decode problem description: `batch` queries of one token each, each against
@@ -111,6 +119,22 @@ typedef struct {
  * decreasing cu_seqlens), E_DIVISIBILITY (L_i % (2*cp) != 0). */
 int cpattn_balanced_split(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t rank,
                           int64_t *positions, int64_t *cu_local);
+
+/* Balanced chunk split of sequences of any length (the padded layout of
+ * cpattn_prefill_desc). Host only. Sequence i of length L_i is padded at its
+ * end to Lp_i = ceil(L_i / (2*cp)) * 2*cp and cut into 2*cp chunks of
+ * c_i = Lp_i / (2*cp) slots; rank `rank` keeps slot chunks `rank` and
+ * 2*cp-1-rank as in cpattn_balanced_split. A slot past L_i is a pad row.
+ *   positions  out, HOST int64 [sum(Lp_i)/cp]: the global packed token index
+ *              cu_seqlens[i] + slot of every local row, or -1 for a pad row.
+ *   cu_local   out, HOST int64 [num_seqs + 1]: local cumulative lengths 2*c_i.
+ * With every L_i divisible by 2*cp the result equals cpattn_balanced_split's.
+ * Padding follows the precedent of the TP/EP design page (tokens that do not
+ * divide evenly are padded; padding takes no part in the outputs).
+ * Errors: E_ARG (null pointer, num_seqs < 0, rank outside [0, cp), cp < 1,
+ * decreasing cu_seqlens). */
+int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t rank,
+                                 int64_t *positions, int64_t *cu_local);
 
 /* One pass-KV ring step of one rank (Definitions table, "Pass-KV", "Ring step",
  * "Partial attention"). Computes, for every local query row of rank `rank`

@@ -21,6 +21,7 @@ from .cp_oracle import (  # noqa: F401
     attention_reference,
     attention_reference_rows,
     balanced_split,
+    balanced_split_padded,
     brute_force_attention,
     canonical,
     decode_reference,
@@ -30,6 +31,7 @@ from .cp_oracle import (  # noqa: F401
     partial_attention,
     passq_decode,
     ring_prefill,
+    ring_prefill_padded,
     ring_schedule,
     sequential_split,
     step_pair_counts,

@@ -95,6 +95,29 @@ def balanced_split(cu_seqlens, cp: int, rank: int) -> Tuple[np.ndarray, np.ndarr
     return np.asarray(pos, dtype=np.int64), np.asarray(cu_local, dtype=np.int64)
 
 
+def balanced_split_padded(cu_seqlens, cp: int, rank: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Balanced chunk split of sequences of any length. Reading taken (the pages
+    fix the split only for lengths divisible by 2*cp; the TP/EP design page pads
+    a token count that does not divide evenly and lets padding take no part in
+    the outputs): a sequence of length L is padded at its end to
+    Lp = ceil(L / (2*cp)) * 2*cp slots and split as one of Lp tokens. Returns the
+    packed global token index of every local slot, -1 for a pad slot, and the
+    local cumulative slot counts."""
+    _check_cp(cp)
+    cu = _cu(cu_seqlens)
+    if not 0 <= rank < cp:
+        raise ValueError("rank out of range")
+    pos: List[int] = []
+    cu_local = [0]
+    for i in range(cu.size - 1):
+        start, L = int(cu[i]), int(cu[i + 1] - cu[i])
+        c = -(-L // (2 * cp))                                     # ceil
+        for first in (rank * c, (2 * cp - 1 - rank) * c):
+            pos.extend(start + x if x < L else -1 for x in range(first, first + c))
+        cu_local.append(cu_local[-1] + 2 * c)
+    return np.asarray(pos, dtype=np.int64), np.asarray(cu_local, dtype=np.int64)
+
+
 def sequential_split(cu_seqlens, cp: int, rank: int) -> np.ndarray:
     """The contrast layout of the Definitions table: rank r holds the r-th
     contiguous 1/cp of every sequence."""
@@ -416,6 +439,38 @@ def ring_prefill(q, k, v, cu_seqlens, cp: int, scale: float, order: Optional[Seq
         o, l = finalize(merge([row[t] for t in steps]))
         out[split[r]] = o
         lse[split[r]] = l
+    return {"partials": partials, "positions": split, "out": out, "lse": lse}
+
+
+def ring_prefill_padded(q, k, v, cu_seqlens, cp: int, scale: float):
+    """ring_prefill over the padded split: pad slots take no part -- a pad slot is
+    no key for anyone, and a pad query slot keeps the identity triple. Returns
+    'partials'[r][t] over every local slot (pad slots included), 'positions'[r]
+    (-1 for pad slots), and 'out' / 'lse' for the real tokens in global order."""
+    cu = _cu(cu_seqlens)
+    seq = _seq_of(cu)
+    T = int(cu[-1])
+    Hq, D = np.asarray(q).shape[1], np.asarray(q).shape[2]
+    split = [balanced_split_padded(cu, cp, r)[0] for r in range(cp)]
+    partials: List[List[Triple]] = []
+    out = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -np.inf)
+    for r in range(cp):
+        rows = split[r]
+        real = rows >= 0
+        row = []
+        for t in range(cp):
+            keys = split[(r - t) % cp]
+            m = np.full((rows.size, Hq), IDENTITY_M)
+            den = np.zeros((rows.size, Hq))
+            num = np.zeros((rows.size, Hq, D))
+            pm, pd, pn = partial_attention(q, k, v, rows[real], keys[keys >= 0], seq, scale, causal=True)
+            m[real], den[real], num[real] = pm, pd, pn
+            row.append((m, den, num))
+        partials.append(row)
+        o, l = finalize(merge(row))
+        out[rows[real]] = o[real]
+        lse[rows[real]] = l[real]
     return {"partials": partials, "positions": split, "out": out, "lse": lse}
 
 

@@ -218,3 +218,23 @@ def test_ring_transfer_entry_points_reject_bad_arguments_without_gpu():
     assert call(vrx=(vp * 2)(base + 4 * block + 16, base + 7 * block)) == ca.E_ARG
     # misaligned block
     assert call(k=(vp * 2)(base + 8, base + block)) == ca.E_ARG
+
+
+@pytest.mark.parametrize("lens,cp", [([5, 13, 0, 1, 7], 2), ([3, 10, 6], 3), ([1, 2, 3, 4, 5, 6, 7, 8, 9], 8),
+                                     ([12464, 15568, 14688, 9376, 15536, 16048], 4), ([1000003], 8)])
+def test_padded_split_matches_oracle(lens, cp):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    for r in range(cp):
+        got_p, got_c = ca.balanced_split_padded(cu, cp, r)
+        want_p, want_c = oracle.balanced_split_padded(cu, cp, r)
+        assert np.array_equal(got_p, want_p) and np.array_equal(got_c, want_c)
+    assert ca.padded_rows(cu, cp) == oracle.balanced_split_padded(cu, cp, 0)[0].size
+
+
+def test_padded_split_errors():
+    with pytest.raises(ca.CpattnError) as e:
+        ca.balanced_split_padded([0, 5, 3], 2, 0)
+    assert e.value.code == ca.E_ARG
+    with pytest.raises(ca.CpattnError) as e:
+        ca.balanced_split_padded([0, 5], 2, 2)
+    assert e.value.code == ca.E_ARG
