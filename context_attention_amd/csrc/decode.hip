@@ -4,15 +4,21 @@
 // (no mask), and the cp triples are reduced (max, denominator, numerator).
 //
 // decode_partial<T, D, G>: streams K and V from HBM. A workgroup owns one
-//   (shard, batch entry, kv head, key split); D/8 lanes share one key row
-//   (16 bytes of bf16 each, so a wavefront load covers whole contiguous rows),
-//   the G query heads of the kv group are scored together and reduced with a
-//   butterfly over those lanes, and every group of lanes keeps its own online
-//   softmax state, merged across lanes and waves once at the end.
-// decode_reduce<D>: one wavefront per (batch entry, query head): folds the
+//   (shard, batch entry, key split, block of G query heads of one kv head);
+//   D/8 lanes share one key row (16 bytes of bf16 each, so a wavefront load
+//   covers whole contiguous rows), the G query heads are scored together and
+//   reduced with a butterfly over those lanes, and every group of lanes keeps its
+//   own online softmax state, merged across lanes and waves once at the end.
+//   Groups of up to 8 query heads per kv head run as one block; larger groups
+//   (multiples of 8) as several blocks of 8 over the same keys.
+// decode_mfma<D>: bf16, groups of 8 or more query heads per kv head (MQA-like
+//   layouts among them): the heads of a kv group are the 32 columns of
+//   S^T = K Q^T and O^T = V^T P^T on the matrix cores (below).
+// decode_reduce<D>: one workgroup per (batch entry, query head): folds the
 //   key splits into the per-shard triples (the partial that rank s would send),
 //   then reduces the cp shard triples into out and lse.
 #include "kernels.h"
+#include "lds_tiles.h"
 
 namespace cpattn {
 namespace {
@@ -33,6 +39,8 @@ struct DecodeArgs {
   int32_t n_hq;
   int32_t n_kv;
   int32_t nsplit;
+  int32_t rep;     // query heads per kv head
+  int32_t n_blk;   // blocks of G query heads: n_hq / G
   int64_t shard_len;
   int64_t split_len;
   float scale;
@@ -80,10 +88,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(DecodeArgs a) {
   const int slot = lane / LPK;
   const int part = lane - slot * LPK;
 
-  // block -> (shard, batch, split, kv head) with the kv head fastest
+  // block -> (shard, batch, split, head block) with the head block fastest
   int64_t bid = blockIdx.x;
-  const int g = (int)(bid % a.n_kv);
-  bid /= a.n_kv;
+  const int hb = (int)(bid % a.n_blk) * G;   // first query head of the block
+  const int g = hb / a.rep;                  // its kv head
+  bid /= a.n_blk;
   const int sp = (int)(bid % a.nsplit);
   bid /= a.nsplit;
   const int bi = (int)(bid % a.batch);
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(DecodeArgs a) {
   // query slice of the G heads, prescaled into the exp2 domain
   float qr[G][8];
   {
-    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)bi * a.n_hq + g * G) * D + part * 8;
+    const T *qp = reinterpret_cast<const T *>(a.q) + ((int64_t)bi * a.n_hq + hb) * D + part * 8;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
       Elem<T>::load8(qp + gg * D, qr[gg]);
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(DecodeArgs a) {
         wt[w] = exp2_fast(red_m[w][gg] - mref);
         lt += wt[w] * red_l[w][gg];
       }
-      const int h = g * G + gg;
+      const int h = hb + gg;
       const int64_t wi = (((int64_t)s * a.batch + bi) * a.n_hq + h) * a.nsplit + sp;
       for (int d = lane; d < D; d += 64) {
         float x = 0.f;
@@ -233,6 +242,317 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(DecodeArgs a) {
       if (lane == 0) {
         a.ws_m[wi] = (mt == kNegInf) ? kNegInf : mt * kLn2;
         a.ws_den[wi] = lt;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// MFMA kernel (bf16, groups of 8 or more query heads per kv head)
+// ----------------------------------------------------------------------------
+// A workgroup owns one (shard, batch entry, key split, kv head) and a block of
+// 32 of the kv head's query heads, which are the 32 columns of S^T = K Q^T and
+// O^T = V^T P^T (v_mfma_f32_32x32x16_bf16); each lane owns one head, so the
+// softmax needs one cross-lane exchange per 32-key tile. Heads past the group
+// are zero columns that are not stored.
+//   head_dim 64 / 128: KG = 4 / 2 waves; wave w streams the split's 32-key tiles
+//     w, w + KG, ... through its own ring of NST = 4 LDS buffers (buffer-to-LDS
+//     copies of whole rows, three tiles in flight while one computes: the HBM
+//     latency is covered by bytes in flight, which the LDS bounds), so the key
+//     loop has no barrier; the KG partial triples are merged through LDS at the
+//     end.
+//   head_dim 512: a quad of waves, each owning a quarter of d and copying only
+//     that quarter of every tile (32 + 64 registers of Q and accumulator); the
+//     four partial score tiles are exchanged through LDS and summed in one fixed
+//     order, so every wave runs the same softmax on identical scores.
+// The column blocks of one key range read the same K and V: with the blocks
+// walked XCD-major they run side by side on one XCD and share its L2.
+template <int D>
+struct DecCfg;
+template <>
+struct DecCfg<64> {
+  static constexpr int DS = 1, KG = 4, NST = 4;
+};
+template <>
+struct DecCfg<128> {
+  static constexpr int DS = 1, KG = 2, NST = 4;
+};
+template <>
+struct DecCfg<512> {
+  static constexpr int DS = 4, KG = 1, NST = 2;
+};
+
+// LDS of decode_mfma<D>: per wave NST buffers of a K and a V tile (32 keys x
+// D/DS columns), the score exchange of a quad (two buffers), and the merge of
+// the KG key groups (aliasing the tiles once the key loop is over).
+template <int D>
+struct DecLds {
+  static constexpr int DS = DecCfg<D>::DS, KG = DecCfg<D>::KG, NST = DecCfg<D>::NST, NW = DS * KG;
+  static constexpr int DQ = D / DS;                        // columns of d per wave
+  static constexpr int TSZ = 32 * DQ;                      // bf16 elements of one K (or V) tile of a wave
+  static constexpr int TILE_BYTES = NW * NST * 2 * TSZ * 2;
+  static constexpr int SX_BYTES = DS > 1 ? 2 * DS * 4 * 64 * 16 : 0;
+  static constexpr int OXS = D + 4;                        // row stride of the merged numerators (floats)
+  static constexpr int MERGE_BYTES = KG > 1 ? KG * 32 * (OXS + 2) * 4 : 0;
+  static constexpr int REGION = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
+  static constexpr int BYTES = REGION + SX_BYTES;
+  static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
+};
+
+struct MfmaArgs {
+  const void *q;
+  const void *k[kMaxShards];
+  const void *v[kMaxShards];
+  float *ws_m;
+  float *ws_den;
+  float *ws_num;
+  int32_t batch;
+  int32_t n_hq;
+  int32_t n_kv;
+  int32_t nsplit;
+  int32_t rep;        // query heads per kv head
+  int32_t ncb;        // 32-head column blocks per kv head
+  int32_t xcd_major;  // 1: the ncb workgroups of one key range sit 8 apart (one XCD)
+  int64_t shard_len;
+  int64_t split_len;
+  float scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * DecCfg<D>::DS * DecCfg<D>::KG) void decode_mfma(MfmaArgs a) {
+  using L = DecLds<D>;
+  constexpr int DS = L::DS, KG = L::KG, NST = L::NST, NW = L::NW, DQ = L::DQ, TSZ = L::TSZ;
+  constexpr int KSQ = DQ / 16;   // QK^T k-steps over a wave's columns
+  constexpr int DBQ = DQ / 32;   // 32-wide blocks of a wave's output columns
+  constexpr int NCH = DQ / 16;   // 1 KB copies per K (or V) tile of a wave
+  constexpr int RPK = 512 / DQ;  // key rows per 1 KB copy
+  constexpr int KCH = DQ / 8;    // 16-byte chunks per row of a wave's columns
+  static_assert((NST - 1) * 2 * NCH <= 63, "copies in flight must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int qi = lane & 31;
+  const int hf = lane >> 5;
+  const int kg = wave / DS, dq = wave % DS;
+
+  // workgroup -> (key range, column block); key range -> (shard, batch, split, kv head)
+  int64_t unit;
+  int cb;
+  {
+    const int64_t b = blockIdx.x;
+    if (a.xcd_major) {
+      const int64_t j = b >> 3;
+      unit = (j / a.ncb) * 8 + (b & 7);
+      cb = (int)(j % a.ncb);
+    } else {
+      unit = b / a.ncb;
+      cb = (int)(b % a.ncb);
+    }
+  }
+  const int g = (int)(unit % a.n_kv);
+  unit /= a.n_kv;
+  const int sp = (int)(unit % a.nsplit);
+  unit /= a.nsplit;
+  const int bi = (int)(unit % a.batch);
+  const int s = (int)(unit / a.batch);
+
+  const int64_t k_begin = (int64_t)sp * a.split_len;
+  const int64_t k_end = min(a.shard_len, k_begin + a.split_len);
+  const int ntile = k_end > k_begin ? (int)((k_end - k_begin + 31) / 32) : 0;
+  const int n_my = ntile > kg ? (ntile - kg + KG - 1) / KG : 0;   // tiles of this key group
+
+  const int hc = cb * 32 + qi;      // this lane's head within the kv group
+  const bool head_ok = hc < a.rep;
+  const int h = g * a.rep + (head_ok ? hc : 0);
+
+  // byte offsets of this lane's 16-byte pieces of a tile (rows of this wave's
+  // columns, chunks placed by the swizzles)
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
+  uint32_t koff[NCH], voff[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int key = i * RPK + lane / KCH;
+    const int pc = lane % KCH;
+    const uint32_t base = key * row_bytes + (uint32_t)((g * D + dq * DQ) * 2);
+    koff[i] = base + (uint32_t)((pc ^ k_swizzle<DQ>(key)) * 16);
+    voff[i] = base + (uint32_t)((pc ^ v_swizzle<DQ>(key)) * 16);
+  }
+  __bf16 *const tiles = reinterpret_cast<__bf16 *>(smem) + wave * NST * 2 * TSZ;   // [buffer][K, V][TSZ]
+  const char *kblk = reinterpret_cast<const char *>(a.k[s]);
+  const char *vblk = reinterpret_cast<const char *>(a.v[s]);
+  const int64_t row0 = (int64_t)bi * a.shard_len;
+  // copies of this wave's tile j into buffer `buf`; past the last tile an empty
+  // range (zeros, no memory touched), so every iteration issues the same count
+  auto issue = [&](int j, int buf) {
+    const bool ok = j < n_my;
+    const int64_t k0 = k_begin + (int64_t)(kg + j * KG) * 32;
+    const int64_t r = ok ? row0 + k0 : 0;
+    const int left = ok ? (int)(k_end - k0) : 0;
+    const u32x4_t rk = uniform_words(tile_words(kblk, r, left, row_bytes));
+    const u32x4_t rv = uniform_words(tile_words(vblk, r, left, row_bytes));
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) dma_1k(koff[i], rk, tiles + (buf * 2) * TSZ + i * 512);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) dma_1k(voff[i], rv, tiles + (buf * 2 + 1) * TSZ + i * 512);
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  const float thr = kRescaleLog2 / sl2;   // rescale threshold in raw-score units
+  float m_ref = kNegInf;                  // reference max of raw scores (this lane's head)
+  float l_run = 0.f;                      // this lane's share of the denominator
+  f32x16_t oacc[DBQ];
+#pragma unroll
+  for (int db = 0; db < DBQ; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  f32x4_t(*Sx)[DS][4][64] = reinterpret_cast<f32x4_t(*)[DS][4][64]>(smem + L::REGION);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[h][dq DQ + 16 ks + 8 hf .. +8]
+  bf16x8_t qf[KSQ];
+  if (n_my > 0) {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) issue(t, t);
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)bi * a.n_hq + h) * D + dq * DQ + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks)
+      qf[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qp + 16 * ks)
+                       : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    // Q and the first NST-1 tiles have landed; waiting here also tells the
+    // compiler that no load of its own is outstanding inside the loop (it
+    // cannot see the copies)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int j = 0; j < n_my; ++j) {
+      const int cur = j % NST;
+      // this wave's reads of tile j-1 have completed before the copies of tile
+      // j+NST-1 overwrite its buffer
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      asm volatile("" ::: "memory");
+      issue(j + NST - 1, (j + NST - 1) % NST);
+      // all but the copies of the NST-1 newer tiles: tile j has landed
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 1) * 2 * NCH));
+      asm volatile("" ::: "memory");
+      const __bf16 *Kc = tiles + (cur * 2) * TSZ;
+      const __bf16 *Vc = tiles + (cur * 2 + 1) * TSZ;
+
+      f32x16_t sacc;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t *>(&Kc[qi * DQ + (((2 * ks + hf) ^ k_swizzle<DQ>(qi)) * 8)]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16_t{} : sacc, 0, 0, 0);
+      }
+      if constexpr (DS > 1) {
+        // full scores: the quad's partials summed in one fixed order
+        put_scores(Sx[j & 1][dq], sacc);
+        __syncthreads();
+        sacc = get_scores(Sx[j & 1][0]);
+#pragma unroll
+        for (int w = 1; w < DS; ++w) sacc += get_scores(Sx[j & 1][w]);
+      }
+      const int64_t k0 = k_begin + (int64_t)(kg + j * KG) * 32;
+      if (k0 + 32 > k_end) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (k0 + kk >= k_end) sacc[r] = kNegInf;
+        }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = max_across_halves(mx);
+      if (__any(mx > m_ref + thr)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBQ; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_ref = m_new;
+      }
+      const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+      uint32_t pk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_fast(fmaf(sacc[r], sl2, -mref));
+        const float p1 = exp2_fast(fmaf(sacc[r + 1], sl2, -mref));
+        pk[r >> 1] = pack_bf16x2(p0, p1);
+        // denominator from the same rounded values the PV product uses
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), ones, l_run, false);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4_t pw = {pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+        for (int db = 0; db < DBQ; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_fragment<DQ>(Vc, ks, db * 32), pf, oacc[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the trailing empty copies have landed too
+  }
+
+  // ---- epilogue: the split's triple of each head (natural-log max)
+  const float l_sum = l_run + __shfl_xor(l_run, 32);
+  const int64_t hrow = ((int64_t)s * a.batch + bi) * a.n_hq + (int64_t)g * a.rep;   // head 0 of the kv group
+  if constexpr (KG == 1) {
+    // the DS waves hold identical statistics; each stores its columns
+    if (head_ok) {
+      const int64_t wi = (hrow + hc) * a.nsplit + sp;
+      if (dq == 0 && hf == 0) {
+        a.ws_m[wi] = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
+        a.ws_den[wi] = l_sum;
+      }
+      float *np = a.ws_num + wi * D + dq * DQ;
+#pragma unroll
+      for (int db = 0; db < DBQ; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4_t *>(np + db * 32 + 8 * g4 + 4 * hf) =
+              f32x4_t{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+    }
+  } else {
+    // merge the KG key groups through LDS (the tile buffers are free now)
+    __syncthreads();
+    float *Ox = reinterpret_cast<float *>(smem);   // [KG][32 heads][OXS]
+    float *Mx = Ox + KG * 32 * L::OXS;              // [KG][32]
+    float *Lx = Mx + KG * 32;                       // [KG][32]
+    float *orow = Ox + (kg * 32 + qi) * L::OXS;
+#pragma unroll
+    for (int db = 0; db < DBQ; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4_t *>(orow + db * 32 + 8 * g4 + 4 * hf) =
+            f32x4_t{oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+    if (hf == 0) {
+      Mx[kg * 32 + qi] = m_ref;
+      Lx[kg * 32 + qi] = l_sum;
+    }
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 64 * NW) {
+      const int n = e / D, d = e - n * D;
+      if (cb * 32 + n >= a.rep) break;   // e only grows: later elements are past the group too
+      float mt = kNegInf;
+#pragma unroll
+      for (int k = 0; k < KG; ++k) mt = fmaxf(mt, Mx[k * 32 + n]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const float mk = Mx[k * 32 + n];
+        const float w = (mk == kNegInf) ? 0.f : exp2_fast((mk - mt) * sl2);
+        num += w * Ox[(k * 32 + n) * L::OXS + d];
+        den += w * Lx[k * 32 + n];
+      }
+      const int64_t wi = (hrow + cb * 32 + n) * a.nsplit + sp;
+      a.ws_num[wi * D + d] = num;
+      if (d == 0) {
+        a.ws_m[wi] = (mt == kNegInf) ? kNegInf : mt * a.scale;
+        a.ws_den[wi] = den;
       }
     }
   }
@@ -253,56 +573,125 @@ struct ReduceArgs {
   int32_t nsplit;
 };
 
+// Wave-wide max and sum (butterfly over the 64 lanes).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+constexpr int kRedWaves = 8;   // waves of a reduce workgroup (shards handled side by side)
+
+// One workgroup per (batch entry, query head). Wave w folds the key splits of
+// shards w, w + 8, ... into the shard triples (written out: the partial rank s
+// would send) and merges them; the waves' results are then merged through LDS.
+// A shard's splits are folded at once: the lanes take the splits' maxima and
+// denominators, the shard max and the split weights follow from two wave
+// reductions, and the numerator is the weighted sum over splits, whose loads
+// are independent of each other.
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce(ReduceArgs a) {
+__global__ __launch_bounds__(64 * kRedWaves) void decode_reduce(ReduceArgs a) {
   constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+  __shared__ float r_m[kRedWaves], r_l[kRedWaves];
+  __shared__ float r_n[kRedWaves][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int64_t item = blockIdx.x;   // bi * n_hq + h
   float tm = kNegInf, tl = 0.f, tacc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) tacc[e] = 0.f;
-  for (int s = 0; s < a.cp; ++s) {
+  for (int s = wave; s < a.cp; s += nw) {
     const int64_t srow = (int64_t)s * a.batch * a.n_hq + item;   // shard-major row
-    float sm = kNegInf, sl = 0.f, sacc[PER];
+    const int64_t w0 = srow * a.nsplit;
+    float sm = kNegInf;
+    for (int c = lane; c < a.nsplit; c += 64) sm = fmaxf(sm, a.ws_m[w0 + c]);
+    sm = wave_max(sm);
+    float sl = 0.f, sacc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) sacc[e] = 0.f;
-    for (int sp = 0; sp < a.nsplit; ++sp) {
-      const int64_t wi = srow * a.nsplit + sp;
-      float mn, w0, w1;
-      merge_weights(sm, a.ws_m[wi], mn, w0, w1);
-      sl = w0 * sl + w1 * a.ws_den[wi];
+    for (int c0 = 0; c0 < a.nsplit; c0 += 64) {
+      const int c = c0 + lane;
+      float wgt = 0.f, dl = 0.f;
+      if (c < a.nsplit) {
+        const float mc = a.ws_m[w0 + c];
+        wgt = (mc == kNegInf) ? 0.f : expf(mc - sm);
+        dl = wgt * a.ws_den[w0 + c];
+      }
+      sl += wave_sum(dl);
+      const int nc = min(64, a.nsplit - c0);
+      const float *np = a.ws_num + (w0 + c0) * D + lane * PER;
+      // eight splits per round: their loads are issued before any is used
+      int i = 0;
+      for (; i + 8 <= nc; i += 8) {
+        float x[8][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) sacc[e] = w0 * sacc[e] + w1 * a.ws_num[wi * D + lane * PER + e];
-      sm = mn;
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) x[u][e] = np[(int64_t)(i + u) * D + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wi = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), i + u));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) sacc[e] = fmaf(wi, x[u][e], sacc[e]);
+        }
+      }
+      for (; i < nc; ++i) {
+        const float wi = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wgt), i));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) sacc[e] = fmaf(wi, np[(int64_t)i * D + e], sacc[e]);
+      }
     }
-    // the shard's partial (what rank s contributes to the reduction)
 #pragma unroll
     for (int e = 0; e < PER; ++e) a.sp_num[srow * D + lane * PER + e] = sacc[e];
     if (lane == 0) {
       a.sp_m[srow] = sm;
       a.sp_den[srow] = sl;
     }
-    float mn, w0, w1;
-    merge_weights(tm, sm, mn, w0, w1);
-    tl = w0 * tl + w1 * sl;
+    float mn, w0t, w1t;
+    merge_weights(tm, sm, mn, w0t, w1t);
+    tl = w0t * tl + w1t * sl;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) tacc[e] = w0 * tacc[e] + w1 * sacc[e];
+    for (int e = 0; e < PER; ++e) tacc[e] = w0t * tacc[e] + w1t * sacc[e];
     tm = mn;
   }
-  const float inv = tl > 0.f ? 1.f / tl : 0.f;
+  if (lane == 0) {
+    r_m[wave] = tm;
+    r_l[wave] = tl;
+  }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) a.out[item * D + lane * PER + e] = tacc[e] * inv;
-  if (lane == 0) a.lse[item] = tl > 0.f ? tm + logf(tl) : kNegInf;
+  for (int e = 0; e < PER; ++e) r_n[wave][lane * PER + e] = tacc[e];
+  __syncthreads();
+  if (wave != 0) return;
+  float fm = kNegInf;
+  for (int w = 0; w < nw; ++w) fm = fmaxf(fm, r_m[w]);
+  float fl = 0.f, facc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) facc[e] = 0.f;
+  for (int w = 0; w < nw; ++w) {
+    const float wt = (r_m[w] == kNegInf) ? 0.f : expf(r_m[w] - fm);
+    fl += wt * r_l[w];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) facc[e] += wt * r_n[w][lane * PER + e];
+  }
+  const float inv = fl > 0.f ? 1.f / fl : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) a.out[item * D + lane * PER + e] = facc[e] * inv;
+  if (lane == 0) a.lse[item] = fl > 0.f ? fm + logf(fl) : kNegInf;
 }
 
-// Split geometry: enough workgroups to fill the chip several times over, and
-// split lengths that are whole numbers of workgroup steps.
-void plan_splits(const cpattn_decode_desc &d, int32_t &nsplit, int64_t &split_len) {
-  const int64_t shard_len = d.kv_len / d.cp;
-  const int64_t step = (int64_t)(64 / (d.head_dim / 8)) * kDecWaves * kUnroll;
-  const int64_t groups = (int64_t)d.cp * d.batch * d.n_kv;
-  int64_t want = (4096 + groups - 1) / groups;
-  int64_t max_by_len = (shard_len + 4 * step - 1) / (4 * step);   // at least 4 steps per split
+// Split geometry: about `target` workgroups over the `groups` (shard, batch
+// entry, head block) triples, at least 4 rounds of `step` keys per split, and
+// split lengths that are whole rounds.
+void plan_splits(int64_t shard_len, int64_t step, int64_t groups, int64_t target, int32_t &nsplit,
+                 int64_t &split_len) {
+  int64_t want = (target + groups - 1) / groups;
+  int64_t max_by_len = (shard_len + 4 * step - 1) / (4 * step);
   if (max_by_len < 1) max_by_len = 1;
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
@@ -312,6 +701,38 @@ void plan_splits(const cpattn_decode_desc &d, int32_t &nsplit, int64_t &split_le
   nsplit = (int32_t)((shard_len + len - 1) / len);
   if (nsplit < 1) nsplit = 1;
   split_len = len;
+}
+
+// The partial kernel a description runs on and its split geometry.
+struct DecodePlan {
+  bool mfma;       // decode_mfma (else decode_partial)
+  int G;           // query heads per kv head
+  int gv;          // decode_partial: query heads per block
+  int ncb;         // decode_mfma: 32-head column blocks per kv head
+  int32_t nsplit;
+  int64_t split_len;
+};
+
+int kg_of(int d) { return d == 64 ? DecCfg<64>::KG : d == 128 ? DecCfg<128>::KG : DecCfg<512>::KG; }
+
+DecodePlan plan_decode(const cpattn_decode_desc &d) {
+  DecodePlan p;
+  p.G = d.n_hq / d.n_kv;
+  // measured on MI355X: at 8 heads per kv head the vector kernel is ALU-bound
+  // (3.6 TB/s on 32/4 heads against 5.7 for decode_mfma); at 4 it streams faster
+  p.mfma = d.dtype == CPATTN_DT_BF16 && p.G >= 8;
+  p.gv = p.G <= 8 ? p.G : 8;
+  p.ncb = (p.G + 31) / 32;
+  const int64_t shard_len = d.kv_len / d.cp;
+  if (p.mfma) {
+    const int64_t groups = (int64_t)d.cp * d.batch * d.n_kv * p.ncb;
+    plan_splits(shard_len, 32LL * kg_of(d.head_dim), groups, 2048, p.nsplit, p.split_len);
+  } else {
+    const int64_t step = (int64_t)(64 / (d.head_dim / 8)) * kDecWaves * kUnroll;
+    const int64_t groups = (int64_t)d.cp * d.batch * (d.n_hq / p.gv);
+    plan_splits(shard_len, step, groups, 4096, p.nsplit, p.split_len);
+  }
+  return p;
 }
 
 template <typename T, int D>
@@ -333,6 +754,18 @@ hipError_t launch_partial(const DecodeArgs &a, int D, int G, int64_t blocks, hip
   return launch_partial_g<T, 512>(a, G, blocks, s);
 }
 
+hipError_t launch_mfma(const MfmaArgs &a, int D, int64_t blocks, hipStream_t s) {
+  if (D == 64)
+    hipLaunchKernelGGL(decode_mfma<64>, dim3((unsigned)blocks), dim3(64 * DecCfg<64>::DS * DecCfg<64>::KG), 0, s, a);
+  else if (D == 128)
+    hipLaunchKernelGGL(decode_mfma<128>, dim3((unsigned)blocks), dim3(64 * DecCfg<128>::DS * DecCfg<128>::KG), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL(decode_mfma<512>, dim3((unsigned)blocks), dim3(64 * DecCfg<512>::DS * DecCfg<512>::KG), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
 }  // namespace
 }  // namespace cpattn
 
@@ -349,12 +782,11 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
   if (d.kv_len % d.cp != 0) return CPATTN_E_DIVISIBILITY;
   if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 512) return CPATTN_E_UNSUPPORTED;
   const int G = d.n_hq / d.n_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return CPATTN_E_UNSUPPORTED;
+  if (!(G == 1 || G == 2 || G == 4 || G % 8 == 0)) return CPATTN_E_UNSUPPORTED;
   if (d.cp > kMaxShards) return CPATTN_E_UNSUPPORTED;
 
-  int32_t nsplit;
-  int64_t split_len;
-  plan_splits(d, nsplit, split_len);
+  const DecodePlan p = plan_decode(d);
+  const int32_t nsplit = p.nsplit;
   const int64_t triples = (int64_t)d.cp * d.batch * d.n_hq * nsplit;
   const size_t need = (size_t)triples * (size_t)(2 + d.head_dim) * sizeof(float);
   if (ws == nullptr) {
@@ -370,34 +802,63 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
     return CPATTN_E_ARG;
   for (int s = 0; s < d.cp; ++s)
     if (d.kv_len > 0 && (k_shards[s] == nullptr || v_shards[s] == nullptr)) return CPATTN_E_ARG;
-  const int64_t blocks = (int64_t)d.cp * d.batch * nsplit * d.n_kv;
+  const int64_t units = (int64_t)d.cp * d.batch * nsplit;
+  const int64_t blocks = p.mfma ? units * d.n_kv * p.ncb : units * (d.n_hq / p.gv);
   if (blocks > 0x7FFFFFFFLL || (int64_t)d.batch * d.n_hq > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
+  if (p.split_len > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
 
-  DecodeArgs a;
-  a.q = q;
-  for (int s = 0; s < d.cp; ++s) {
-    a.k[s] = k_shards[s];
-    a.v[s] = v_shards[s];
-  }
   float *wsf = reinterpret_cast<float *>(ws);
-  a.ws_m = wsf;
-  a.ws_den = wsf + triples;
-  a.ws_num = wsf + 2 * triples;
-  a.batch = d.batch;
-  a.n_hq = d.n_hq;
-  a.n_kv = d.n_kv;
-  a.nsplit = nsplit;
-  a.shard_len = d.kv_len / d.cp;
-  a.split_len = split_len;
-  a.scale = d.scale;
-  hipError_t e = d.dtype == CPATTN_DT_BF16 ? launch_partial<__bf16>(a, d.head_dim, G, blocks, stream)
-                                           : launch_partial<float>(a, d.head_dim, G, blocks, stream);
+  float *ws_m = wsf, *ws_den = wsf + triples, *ws_num = wsf + 2 * triples;
+  hipError_t e;
+  if (p.mfma) {
+    MfmaArgs a;
+    a.q = q;
+    for (int s = 0; s < d.cp; ++s) {
+      a.k[s] = k_shards[s];
+      a.v[s] = v_shards[s];
+    }
+    a.ws_m = ws_m;
+    a.ws_den = ws_den;
+    a.ws_num = ws_num;
+    a.batch = d.batch;
+    a.n_hq = d.n_hq;
+    a.n_kv = d.n_kv;
+    a.nsplit = nsplit;
+    a.rep = G;
+    a.ncb = p.ncb;
+    a.xcd_major = (p.ncb > 1 && (units * d.n_kv) % 8 == 0) ? 1 : 0;
+    a.shard_len = d.kv_len / d.cp;
+    a.split_len = p.split_len;
+    a.scale = d.scale;
+    e = launch_mfma(a, d.head_dim, blocks, stream);
+  } else {
+    DecodeArgs a;
+    a.q = q;
+    for (int s = 0; s < d.cp; ++s) {
+      a.k[s] = k_shards[s];
+      a.v[s] = v_shards[s];
+    }
+    a.ws_m = ws_m;
+    a.ws_den = ws_den;
+    a.ws_num = ws_num;
+    a.batch = d.batch;
+    a.n_hq = d.n_hq;
+    a.n_kv = d.n_kv;
+    a.nsplit = nsplit;
+    a.rep = G;
+    a.n_blk = d.n_hq / p.gv;
+    a.shard_len = d.kv_len / d.cp;
+    a.split_len = p.split_len;
+    a.scale = d.scale;
+    e = d.dtype == CPATTN_DT_BF16 ? launch_partial<__bf16>(a, d.head_dim, p.gv, blocks, stream)
+                                  : launch_partial<float>(a, d.head_dim, p.gv, blocks, stream);
+  }
   if (e != hipSuccess) return CPATTN_E_DEVICE;
 
   ReduceArgs r;
-  r.ws_m = a.ws_m;
-  r.ws_den = a.ws_den;
-  r.ws_num = a.ws_num;
+  r.ws_m = ws_m;
+  r.ws_den = ws_den;
+  r.ws_num = ws_num;
   r.sp_m = shard_partials->m;
   r.sp_den = shard_partials->den;
   r.sp_num = shard_partials->num;
@@ -408,9 +869,10 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
   r.n_hq = d.n_hq;
   r.nsplit = nsplit;
   const unsigned rb = (unsigned)((int64_t)d.batch * d.n_hq);
-  if (d.head_dim == 64) hipLaunchKernelGGL(decode_reduce<64>, dim3(rb), dim3(64), 0, stream, r);
-  else if (d.head_dim == 128) hipLaunchKernelGGL(decode_reduce<128>, dim3(rb), dim3(64), 0, stream, r);
-  else hipLaunchKernelGGL(decode_reduce<512>, dim3(rb), dim3(64), 0, stream, r);
+  const dim3 rt(64 * (d.cp < kRedWaves ? d.cp : kRedWaves));
+  if (d.head_dim == 64) hipLaunchKernelGGL(decode_reduce<64>, dim3(rb), rt, 0, stream, r);
+  else if (d.head_dim == 128) hipLaunchKernelGGL(decode_reduce<128>, dim3(rb), rt, 0, stream, r);
+  else hipLaunchKernelGGL(decode_reduce<512>, dim3(rb), rt, 0, stream, r);
   if (hipGetLastError() != hipSuccess) return CPATTN_E_DEVICE;
   return CPATTN_OK;
 }

@@ -19,10 +19,11 @@
 //       and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
 //       every lane owns one query column of both products and the softmax needs a
 //       single cross-lane exchange per tile.
-//   ring_step_wide<HG>  bf16, head_dim 512: wave pairs split d (below).
+//   ring_step_wide<HG>  bf16, head_dim 512: wave quads split d (below).
 //   ring_step_generic<T, D>  fp32: one workgroup per (query row, query head),
 //       fp32 arithmetic throughout.
 #include "kernels.h"
+#include "lds_tiles.h"
 
 namespace cpattn {
 namespace {
@@ -79,7 +80,7 @@ __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, f
 // 32-row blocks per wave (NB) and waves per SIMD (WPE). head_dim 64/128: 8
 // waves, two per SIMD, so one wave's MFMAs overlap the other's softmax and
 // latencies (a wave per SIMD with two row blocks halves LDS reads per MFMA but
-// measured half the speed). head_dim 512 runs ring_step_wide (wave pairs split d).
+// measured half the speed). head_dim 512 runs ring_step_wide (wave quads split d).
 template <int D>
 struct Cfg;
 template <>
@@ -97,27 +98,6 @@ struct Cfg<512> {
 };
 template <int D>
 constexpr int kThreadsOf = 64 * Cfg<D>::NW;
-// Rescale threshold of the running max in the exp2 domain: the numerator and
-// denominator are only rescaled when the max grows by more than 2^8, so
-// exp2(s - m_ref) stays below 256.
-constexpr float kRescaleLog2 = 8.0f;
-
-// K and V tiles sit in LDS as they are in HBM, [key][d] bf16, with the 16-byte
-// chunks of each row permuted (chunk c of row r at position c ^ swizzle(r)).
-//   K: read as the A operand of S^T = K Q^T, 16 bytes of one row per lane, 32
-//     consecutive rows per wave; k_swizzle spreads 16 consecutive rows of one
-//     chunk over 16 distinct bank groups.
-//   V: read transposed by ds_read_b64_tr_b16 (below); a 16-lane group reads 8
-//     bytes from each of 4 consecutive rows, and v_swizzle puts those 4 rows on
-//     disjoint banks whether the LDS serves 32 or 64 banks per cycle.
-template <int D>
-__device__ __forceinline__ int k_swizzle(int row) {
-  return (D == 64) ? ((row >> 1) & 7) : (row & 15);
-}
-template <int D>
-__device__ __forceinline__ int v_swizzle(int row) {
-  return (D == 64) ? 2 * (row & 3) : 4 * (row & 1) + 10 * ((row >> 1) & 1);
-}
 
 // Per-thread byte offsets (relative to the first key row of a tile) of the
 // buffer-to-LDS copies of a K and a V tile. Lane L of a wave writes bytes
@@ -132,9 +112,6 @@ struct StageMap {
   uint32_t k[KN];
   uint32_t v[KN];
 };
-
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer resource word 3 on gfx9
-constexpr int kWaitVmcnt0 = 0x0F70;              // s_waitcnt vmcnt(0), other counters unconstrained
 
 template <int D>
 __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
@@ -154,70 +131,14 @@ __device__ __forceinline__ StageMap<D> stage_map(uint32_t row_bytes, int g) {
   return o;
 }
 
-// Buffer resource of a tile: base at key row `row`, loads at or past
-// rows_left * row_bytes return zeros.
-__device__ __forceinline__ u32x4_t tile_words(const char *block, int64_t row, int rows_left, uint32_t row_bytes) {
-  const int64_t lim = (int64_t)rows_left * row_bytes;
-  const uint32_t nrec = (uint32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
-  const uint64_t base = (uint64_t)(block + row * (int64_t)row_bytes);
-  return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, kBufferWord3};
-}
-
-// Starts the copy of a tile straight into its LDS buffer (buffer_load ... lds,
-// 16 bytes per lane, M0 = the wave's 1 KB destination). The copy is written as
-// inline assembly on purpose: the compiler tracks its own buffer-to-LDS copies
-// and, unable to tell LDS ranges apart, makes the first LDS read after one wait
-// for every outstanding vector load, which would expose the whole load latency
-// at the top of each tile. The kernels wait for these copies themselves
-// (vmcnt(0) before the barrier that publishes the tile).
+// Starts the copies of a tile straight into its LDS buffer: the wave's KN
+// chunks of 1 KB.
 template <int D>
 __device__ __forceinline__ void load_tile(const uint32_t (&off)[StageMap<D>::KN], u32x4_t rsrc, __bf16 *dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
   const int wave = threadIdx.x >> 6;
-  // the resource is uniform; readfirstlane keeps it in scalar registers
-  const u32x4_t rs = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]),
-                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
-                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]),
-                      (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  const u32x4_t rs = uniform_words(rsrc);
 #pragma unroll
-  for (int i = 0; i < StageMap<D>::KN; ++i) {
-    __bf16 *chunk = dst + (wave * StageMap<D>::KN + i) * 512;   // 1 KB
-    const uint32_t lds =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)chunk);
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off[i]), "s"(rs), "{m0}"(lds));
-  }
-#endif
-}
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-// A operand of O^T = V^T P^T for k-step ks (16 keys) and the 32 head-dim
-// columns [d0, d0 + 32): lane (m = lane % 32, h = lane / 32) needs V[key][d0 + m]
-// for the keys 16 ks + 4 h + {0..3} (elements 0..3) and 16 ks + 8 + 4 h + {0..3}
-// (elements 4..7), the order in which the S^T accumulator lays out the keys of
-// the P fragment. ds_read_b64_tr_b16 gives lane i of a 16-lane group element e
-// of the 8 bytes addressed by lane 4e + i/4, so when lane j of the group
-// addresses row k0 + j/4 at column c0 + 4 (j % 4), lane i receives
-// V[k0 .. k0 + 3][c0 + i]: one read per 4 keys, the second 8 rows further on.
-// d0 must be a multiple of 32.
-template <int D>
-__device__ __forceinline__ bf16x8_t v_fragment(const __bf16 *Vc, int ks, int d0) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15;
-  const int row = 16 * ks + 4 * (lane >> 5) + (j >> 2);
-  const int col = d0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const int off = row * D + 8 * ((col >> 3) ^ v_swizzle<D>(row)) + (col & 7);   // rows +8 share the swizzle
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const lds_i16x4 *p = (const lds_i16x4 *)(Vc + off);
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 2 * D));
-  const i16x4_t both[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8_t, both);
-#else
-  (void)Vc; (void)ks; (void)d0;
-  return bf16x8_t{};
-#endif
+  for (int i = 0; i < StageMap<D>::KN; ++i) dma_1k(off[i], rs, dst + (wave * StageMap<D>::KN + i) * 512);
 }
 
 // Work unit and head group of a workgroup. When the head groups come in
@@ -579,7 +500,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// head_dim 512 (bf16): wave pairs split d.
+// head_dim 512 (bf16): wave quads split d.
 // ----------------------------------------------------------------------------
 // A workgroup of 8 waves (two per SIMD) is two groups of NS = 4; the waves of a
 // group own the same 32 query rows and a quarter of d each: Q and the output
@@ -590,26 +511,6 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 // hold bit-identical scores and run the same softmax; the PV product then fills
 // each wave's quarter of the output. Keys come in 32-key tiles copied straight
 // into double-buffered LDS (2 x 32 KB for K and for V, 32 KB of partial scores).
-__device__ __forceinline__ void put_scores(f32x4_t (*x)[64], const f32x16_t &s) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) x[g][lane] = f32x4_t{s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]};
-}
-
-__device__ __forceinline__ f32x16_t get_scores(const f32x4_t (*x)[64]) {
-  const int lane = threadIdx.x & 63;
-  f32x16_t s;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4_t t = x[g][lane];
-    s[4 * g] = t[0];
-    s[4 * g + 1] = t[1];
-    s[4 * g + 2] = t[2];
-    s[4 * g + 3] = t[3];
-  }
-  return s;
-}
-
 template <int HG>
 __global__ __launch_bounds__(kThreadsOf<512>) __attribute__((amdgpu_waves_per_eu(Cfg<512>::WPE, Cfg<512>::WPE)))
 void ring_step_wide(SeqTable tab, StepArgs a) {
@@ -993,7 +894,7 @@ hipError_t launch_wide(const SeqTable &t, const StepArgs &a, int units, hipStrea
 }
 
 // heads per workgroup: up to 4 query heads of one kv group (2 for head_dim 512,
-// whose workgroup holds two wave pairs)
+// whose workgroup holds two wave quads)
 int pick_hg_d(int d, int rep) {
   const int hg = pick_hg(rep);
   return (d == 512 && hg > 2) ? 2 : hg;

@@ -222,6 +222,9 @@ int cpattn_merge(int64_t rows, int32_t n_hq, int32_t head_dim,
  * keys (no mask), and the cp shard triples are reduced into the result.
  *   q         device [batch, n_hq, head_dim].
  *   k_shards, v_shards  HOST arrays of cp device pointers, each [batch, kv_len/cp, n_kv, head_dim].
+ *             Query heads per kv head, n_hq / n_kv: 1, 2, 4 or any multiple of 8
+ *             (n_kv = 1 with many query heads is the MQA layout that compressed-KV
+ *             schemes such as MLA decode with); E_UNSUPPORTED otherwise.
  *   shard_partials  device triple with rows = cp*batch (shard-major: row s*batch + b):
  *             the per-shard triples, written by this call.
  *   out       device fp32 [batch, n_hq, head_dim];  lse device fp32 [batch, n_hq].

@@ -167,6 +167,15 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
                          scale=0.1)
     assert lib.cpattn_passq_decode(ctypes.byref(bad), None, None, None, None, None, None, None,
                                    ctypes.byref(n), None) == ca.E_UNSUPPORTED
+    # query heads per kv head: 1, 2, 4 or a multiple of 8 (MQA-like groups included)
+    for n_hq, n_kv, code in ((48, 8, ca.E_UNSUPPORTED), (12, 1, ca.E_UNSUPPORTED), (16, 1, ca.OK),
+                             (128, 1, ca.OK), (64, 2, ca.OK), (40, 1, ca.OK)):
+        for dt in (ca.DT_BF16, ca.DT_F32):
+            dq = ca._DecodeDesc(batch=2, cp=4, kv_len=4096, n_hq=n_hq, n_kv=n_kv, head_dim=512, dtype=dt, scale=0.1)
+            assert lib.cpattn_passq_decode(ctypes.byref(dq), None, None, None, None, None, None, None,
+                                           ctypes.byref(n), None) == code, (n_hq, n_kv, dt)
+            if code == ca.OK:   # one triple of 2 + head_dim floats per (shard, batch, head, split)
+                assert n.value % (4 * 2 * n_hq * (2 + 512) * 4) == 0 and n.value > 0
 
 
 def test_ring_transfer_entry_points_reject_bad_arguments_without_gpu():

@@ -20,6 +20,16 @@ CASES = [
     ("gqa2-bf16-d512-cp4", 2, 4 * 300, 4, 4, 2, 512, "bf16"),
     ("gqa4-f32-d64-cp2", 2, 2 * 500, 2, 4, 1, 64, "f32"),
     ("tiny-keys-bf16-cp8", 1, 8, 8, 4, 2, 128, "bf16"),
+    # groups of 16 or more query heads per kv head (MQA-like; bf16 runs decode_mfma)
+    ("mqa32-bf16-d128-ragged-tiles", 2, 4 * 1000, 4, 32, 1, 128, "bf16"),
+    ("mqa16-bf16-d64-half-block", 2, 2 * 777, 2, 16, 1, 64, "bf16"),
+    ("mqa48-bf16-d64-two-blocks", 2, 2 * 5000, 2, 48, 1, 64, "bf16"),
+    ("mla-like-128-bf16-d512-cp4", 2, 4 * 300, 4, 128, 1, 512, "bf16"),
+    ("mqa40-bf16-d512-cp1", 1, 3000, 1, 40, 1, 512, "bf16"),
+    ("gqa32-bf16-d128-two-kv-heads", 3, 8 * 640, 8, 64, 2, 128, "bf16"),
+    ("mqa32-bf16-one-key-shards", 1, 8, 8, 32, 1, 128, "bf16"),
+    ("mqa16-f32-d128-head-blocks", 2, 2 * 500, 2, 16, 1, 128, "f32"),
+    ("gqa16-f32-d64-two-kv-heads", 2, 2 * 300, 2, 32, 2, 64, "f32"),
 ]
 
 

@@ -30,6 +30,10 @@ CASES = [
     ("gqa2-f32-d512", [2 * 2 * 12], 2, 2, 1, 512, "f32", 1.0),
     ("cp1-bf16-d128", [300, 64], 1, 8, 2, 128, "bf16", 0.5),
     ("cp8-bf16-d128-mqa", [2 * 8 * 40], 8, 4, 1, 128, "bf16", 0.5),
+    # one kv head shared by many query heads (MQA; MLA-like at head_dim 512)
+    ("mqa32-bf16-d128-cp4", [2 * 4 * 96, 2 * 4 * 17], 4, 32, 1, 128, "bf16", 0.5),
+    ("mqa64-bf16-d512-cp2", [2 * 2 * 40], 2, 64, 1, 512, "bf16", 0.5),
+    ("mqa16-bf16-d64-cp2", [2 * 2 * 75], 2, 16, 1, 64, "bf16", 0.5),
     ("empty-seqs-bf16", [0, 2 * 2 * 33, 0], 2, 4, 2, 64, "bf16", 0.5),
 ]
 
