@@ -573,6 +573,238 @@ struct ReduceArgs {
   int32_t nsplit;
 };
 
+// ----------------------------------------------------------------------------
+// MFMA kernel for many query heads per kv head (bf16, more than 32)
+// ----------------------------------------------------------------------------
+// A workgroup owns one (shard, batch entry, key split, kv head) and up to 16 NW
+// of the kv head's query heads (NW = 8, or 4 at head_dim 512): wave w takes 16 of them, which are the 16
+// columns of S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16, each
+// over the full head_dim (head_dim 512: 64 registers of Q and 128 of
+// accumulator, no exchange between waves). The NW waves share every 32-key K
+// and V tile in LDS, copied once per workgroup by all of them together, so each
+// key is read from HBM once for all the heads of the workgroup. Lane l holds
+// head l % 16; its 16-lane group g = l / 16 holds keys 4 g + {0..3} and
+// 16 + 4 g + {0..3} of a tile, in the (group, element) order that the P and V
+// operands of the PV product share.
+// Keys per LDS stage (TK) and stages (NST). At head_dim 512 a stage takes
+// 64 KB, so two fit. Measured on MI355X at 128/1 heads, head_dim 512: 16-key
+// stages (five fit; PV on v_mfma_f32_16x16x16_bf16) were 47% slower, and the
+// kernel is limited by the matrix work of its single wave per SIMD rather than
+// by bytes in flight.
+template <int D>
+struct Dec16Cfg;
+template <>
+struct Dec16Cfg<64> {
+  static constexpr int TK = 32, NST = 4;
+};
+template <>
+struct Dec16Cfg<128> {
+  static constexpr int TK = 32, NST = 4;
+};
+template <>
+struct Dec16Cfg<512> {
+  static constexpr int TK = 32, NST = 2;
+};
+
+// Chunk permutation of a V tile for the transposed reads of this kernel: the
+// 16 rows one read touches land on distinct banks (checked for 32- and 64-bank
+// LDS).
+template <int D>
+__device__ __forceinline__ int v16_swizzle(int row) {
+  return (D == 64) ? 2 * ((row ^ (row >> 2)) & 1) + 4 * ((row >> 1) & 1) : 2 * (row & 7);
+}
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mfma16(MfmaArgs a) {
+  constexpr int NST = Dec16Cfg<D>::NST;
+  constexpr int TK = Dec16Cfg<D>::TK;          // keys per tile
+  constexpr int TSZ = TK * D;                  // bf16 elements of a K (or V) tile
+  constexpr int CH = TSZ * 2 / 1024;           // 1 KB copies per K (or V) tile
+  constexpr int CPW = CH >= NW ? CH / NW : 1;  // copies per wave (waves past CH repeat a chunk)
+  constexpr int RPK = 512 / D;                 // key rows per 1 KB copy
+  constexpr int KCH = D / 8;                   // 16-byte chunks per row
+  constexpr int KS = D / 32;                   // QK^T k-steps
+  constexpr int DB = D / 16;                   // 16-row blocks of O^T
+  static_assert(CH % NW == 0 || NW % CH == 0, "copies split evenly over the waves");
+  static_assert((NST - 1) * 2 * CPW <= 63, "copies in flight must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(16))) __bf16 Kt[NST][TSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[NST][TSZ];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;     // head of this lane within the wave's 16
+  const int grp = lane >> 4;     // 16-lane group
+
+  int64_t unit;
+  int hs;
+  {
+    const int64_t b = blockIdx.x;
+    if (a.xcd_major) {
+      const int64_t j = b >> 3;
+      unit = (j / a.ncb) * 8 + (b & 7);
+      hs = (int)(j % a.ncb);
+    } else {
+      unit = b / a.ncb;
+      hs = (int)(b % a.ncb);
+    }
+  }
+  const int g = (int)(unit % a.n_kv);
+  unit /= a.n_kv;
+  const int sp = (int)(unit % a.nsplit);
+  unit /= a.nsplit;
+  const int bi = (int)(unit % a.batch);
+  const int s = (int)(unit / a.batch);
+
+  const int64_t k_begin = (int64_t)sp * a.split_len;
+  const int64_t k_end = min(a.shard_len, k_begin + a.split_len);
+  const int ntile = k_end > k_begin ? (int)((k_end - k_begin + TK - 1) / TK) : 0;
+
+  const int hb0 = (hs * NW + wave) * 16;     // first head of this wave within the kv group
+  const bool wave_on = hb0 < a.rep;           // the wave has heads (uniform)
+  const int hc = hb0 + col;
+  const bool head_ok = hc < a.rep;
+  const int h = g * a.rep + (head_ok ? hc : 0);
+
+  // copy offsets: chunk q of a tile holds key rows q RPK .. q RPK + RPK - 1
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
+  uint32_t koff[CPW], voff[CPW];
+  int kq[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int q = (wave * CPW + i) % CH;
+    kq[i] = q;
+    const int key = q * RPK + lane / KCH;
+    const int pc = lane % KCH;
+    const uint32_t base = key * row_bytes + (uint32_t)(g * D * 2);
+    koff[i] = base + (uint32_t)((pc ^ k_swizzle<D>(key)) * 16);
+    voff[i] = base + (uint32_t)((pc ^ v16_swizzle<D>(key)) * 16);
+  }
+  static_assert(CH * RPK == TK, "the copies of a tile cover its key rows");
+  const char *kblk = reinterpret_cast<const char *>(a.k[s]);
+  const char *vblk = reinterpret_cast<const char *>(a.v[s]);
+  const int64_t row0 = (int64_t)bi * a.shard_len;
+  auto issue = [&](int j, int buf) {
+    const bool ok = j < ntile;
+    const int64_t k0 = k_begin + (int64_t)j * TK;
+    const int64_t r = ok ? row0 + k0 : 0;
+    const int left = ok ? (int)(k_end - k0) : 0;
+    const u32x4_t rk = uniform_words(tile_words(kblk, r, left, row_bytes));
+    const u32x4_t rv = uniform_words(tile_words(vblk, r, left, row_bytes));
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) dma_1k(koff[i], rk, &Kt[buf][kq[i] * 512]);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) dma_1k(voff[i], rv, &Vt[buf][kq[i] * 512]);
+  };
+
+  const float sl2 = a.scale * kLog2e;
+  const float thr = kRescaleLog2 / sl2;
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4v_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4v_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[h][32 ks + 8 grp .. +8]
+  bf16x8_t qf[KS];
+  if (ntile > 0) {
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) issue(t, t);
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)bi * a.n_hq + h) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qp + 32 * ks)
+                       : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int j = 0; j < ntile; ++j) {
+      const int cur = j % NST;
+      // this wave's copies of tile j have landed (those of the NST-2 newer tiles
+      // may still fly); after the barrier every wave's have, and every wave is
+      // done with the buffer that tile j+NST-1 goes into (tile j-1's)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * 2 * CPW));
+      __syncthreads();
+      issue(j + NST - 1, (j + NST - 1) % NST);
+      if (!wave_on) continue;
+      const __bf16 *Kc = Kt[cur];
+      f32x4v_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 4 * ks + grp;
+        const int r0 = col, r1 = 16 + col;
+        const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(&Kc[r0 * D + ((ch ^ k_swizzle<D>(r0)) * 8)]);
+        const bf16x8_t k1f = *reinterpret_cast<const bf16x8_t *>(&Kc[r1 * D + ((ch ^ k_swizzle<D>(r1)) * 8)]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0f, qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1f, qf[ks], s1, 0, 0, 0);
+      }
+      const int64_t k0 = k_begin + (int64_t)j * TK;
+      if (k0 + 32 > k_end) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (k0 + 4 * grp + t >= k_end) s0[t] = kNegInf;
+          if (k0 + 16 + 4 * grp + t >= k_end) s1[t] = kNegInf;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = max_across_halves(mx);
+      if (__any(mx > m_ref + thr)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_ref = m_new;
+      }
+      const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+      uint32_t pk[4];
+      pk[0] = pack_bf16x2(exp2_fast(fmaf(s0[0], sl2, -mref)), exp2_fast(fmaf(s0[1], sl2, -mref)));
+      pk[1] = pack_bf16x2(exp2_fast(fmaf(s0[2], sl2, -mref)), exp2_fast(fmaf(s0[3], sl2, -mref)));
+      pk[2] = pack_bf16x2(exp2_fast(fmaf(s1[0], sl2, -mref)), exp2_fast(fmaf(s1[1], sl2, -mref)));
+      pk[3] = pack_bf16x2(exp2_fast(fmaf(s1[2], sl2, -mref)), exp2_fast(fmaf(s1[3], sl2, -mref)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, l_run, false);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+      // V^T operand: lane (d row = col, group) needs V[4 grp + 0..3][16 db + col]
+      // and V[16 + 4 grp + 0..3][16 db + col]: two transposed reads
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int row = 4 * grp + (col >> 2);
+        const int cc = 16 * db + 4 * (col & 3);
+        const int off = row * D + 8 * ((cc >> 3) ^ v16_swizzle<D>(row)) + (cc & 7);   // rows +16 share the swizzle
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+        const lds_i16x4 *vp = (const lds_i16x4 *)(Vt[cur] + off);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)vp);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 4 * D));
+        const i16x4_t both[2] = {lo, hi};
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, both);
+#else
+        const bf16x8_t vf = {};
+#endif
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
+      }
+        }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the trailing empty copies have landed
+  }
+
+  // ---- epilogue: the split's triple of each head (natural-log max)
+  float l_sum = l_run + __shfl_xor(l_run, 16);
+  l_sum += __shfl_xor(l_sum, 32);
+  if (head_ok) {
+    const int64_t wi = ((((int64_t)s * a.batch + bi) * a.n_hq + (int64_t)g * a.rep) + hc) * a.nsplit + sp;
+    if (grp == 0) {
+      a.ws_m[wi] = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
+      a.ws_den[wi] = l_sum;
+    }
+    float *np = a.ws_num + wi * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4v_t *>(np + 16 * db) = oacc[db];
+  }
+}
+
 // Wave-wide max and sum (butterfly over the 64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -706,9 +938,11 @@ void plan_splits(int64_t shard_len, int64_t step, int64_t groups, int64_t target
 // The partial kernel a description runs on and its split geometry.
 struct DecodePlan {
   bool mfma;       // decode_mfma (else decode_partial)
+  bool mfma16;     // decode_mfma16 (takes precedence)
   int G;           // query heads per kv head
   int gv;          // decode_partial: query heads per block
-  int ncb;         // decode_mfma: 32-head column blocks per kv head
+  int ncb;         // decode_mfma: 32-head column blocks per kv head; decode_mfma16: head blocks of 16 NW
+  int nw;          // decode_mfma16: waves per workgroup
   int32_t nsplit;
   int64_t split_len;
 };
@@ -721,10 +955,22 @@ DecodePlan plan_decode(const cpattn_decode_desc &d) {
   // measured on MI355X: at 8 heads per kv head the vector kernel is ALU-bound
   // (3.6 TB/s on 32/4 heads against 5.7 for decode_mfma); at 4 it streams faster
   p.mfma = d.dtype == CPATTN_DT_BF16 && p.G >= 8;
+  // more than 32 heads per kv head: one workgroup serves up to 128 of them from
+  // one copy of each K and V tile
+  p.mfma16 = d.dtype == CPATTN_DT_BF16 && p.G > 32;
   p.gv = p.G <= 8 ? p.G : 8;
   p.ncb = (p.G + 31) / 32;
+  p.nw = 0;
   const int64_t shard_len = d.kv_len / d.cp;
-  if (p.mfma) {
+  if (p.mfma16) {
+    const int blk16 = (p.G + 15) / 16;
+    // head_dim 512 keeps 4 waves (one per SIMD): 8 would not fit their Q and
+    // accumulators in the registers of two waves per SIMD
+    p.nw = (blk16 >= 8 && d.head_dim != 512) ? 8 : 4;
+    p.ncb = (blk16 + p.nw - 1) / p.nw;
+    const int64_t groups = (int64_t)d.cp * d.batch * d.n_kv * p.ncb;
+    plan_splits(shard_len, 32, groups, 2048, p.nsplit, p.split_len);
+  } else if (p.mfma) {
     const int64_t groups = (int64_t)d.cp * d.batch * d.n_kv * p.ncb;
     plan_splits(shard_len, 32LL * kg_of(d.head_dim), groups, 2048, p.nsplit, p.split_len);
   } else {
@@ -752,6 +998,20 @@ hipError_t launch_partial(const DecodeArgs &a, int D, int G, int64_t blocks, hip
   if (D == 64) return launch_partial_g<T, 64>(a, G, blocks, s);
   if (D == 128) return launch_partial_g<T, 128>(a, G, blocks, s);
   return launch_partial_g<T, 512>(a, G, blocks, s);
+}
+
+hipError_t launch_mfma16(const MfmaArgs &a, int D, int nw, int64_t blocks, hipStream_t s) {
+  const dim3 grid((unsigned)blocks), block(64 * nw);
+  if (D == 64) {
+    if (nw == 8) hipLaunchKernelGGL((decode_mfma16<64, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_mfma16<64, 4>), grid, block, 0, s, a);
+  } else if (D == 128) {
+    if (nw == 8) hipLaunchKernelGGL((decode_mfma16<128, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_mfma16<128, 4>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_mfma16<512, 4>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma(const MfmaArgs &a, int D, int64_t blocks, hipStream_t s) {
@@ -803,14 +1063,14 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
   for (int s = 0; s < d.cp; ++s)
     if (d.kv_len > 0 && (k_shards[s] == nullptr || v_shards[s] == nullptr)) return CPATTN_E_ARG;
   const int64_t units = (int64_t)d.cp * d.batch * nsplit;
-  const int64_t blocks = p.mfma ? units * d.n_kv * p.ncb : units * (d.n_hq / p.gv);
+  const int64_t blocks = (p.mfma || p.mfma16) ? units * d.n_kv * p.ncb : units * (d.n_hq / p.gv);
   if (blocks > 0x7FFFFFFFLL || (int64_t)d.batch * d.n_hq > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
   if (p.split_len > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
 
   float *wsf = reinterpret_cast<float *>(ws);
   float *ws_m = wsf, *ws_den = wsf + triples, *ws_num = wsf + 2 * triples;
   hipError_t e;
-  if (p.mfma) {
+  if (p.mfma || p.mfma16) {
     MfmaArgs a;
     a.q = q;
     for (int s = 0; s < d.cp; ++s) {
@@ -830,7 +1090,7 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
     a.shard_len = d.kv_len / d.cp;
     a.split_len = p.split_len;
     a.scale = d.scale;
-    e = launch_mfma(a, d.head_dim, blocks, stream);
+    e = p.mfma16 ? launch_mfma16(a, d.head_dim, p.nw, blocks, stream) : launch_mfma(a, d.head_dim, blocks, stream);
   } else {
     DecodeArgs a;
     a.q = q;

@@ -28,6 +28,10 @@ CASES = [
     ("mqa40-bf16-d512-cp1", 1, 3000, 1, 40, 1, 512, "bf16"),
     ("gqa32-bf16-d128-two-kv-heads", 3, 8 * 640, 8, 64, 2, 128, "bf16"),
     ("mqa32-bf16-one-key-shards", 1, 8, 8, 32, 1, 128, "bf16"),
+    # more than 32 query heads per kv head (bf16 runs decode_mfma16)
+    ("gqa128-bf16-d128-8-waves", 2, 4 * 100, 4, 256, 2, 128, "bf16"),
+    ("mqa96-bf16-d64-partial-head-blocks", 2, 2 * 777, 2, 96, 1, 64, "bf16"),
+    ("mqa64-bf16-one-key-shards", 1, 8, 8, 64, 1, 128, "bf16"),
     ("mqa16-f32-d128-head-blocks", 2, 2 * 500, 2, 16, 1, 128, "f32"),
     ("gqa16-f32-d64-two-kv-heads", 2, 2 * 300, 2, 32, 2, 64, "f32"),
 ]
