@@ -131,12 +131,110 @@ def overlap_report(ca, synth, torch, pdesc, q0, blocks):
             "middle_band": dict(workload="MHA 64 heads, d128, S=16384, cp=8, rank 3", **rnd(band))}
 
 
+def _full_ring_tflops(ca, synth, torch, w, reps=3):
+    """Every rank's full ring (cp fused ring steps per rank, then finalize) of a
+    prefill workload: exact causal FLOPs of all cp^2 ring-step launches / their
+    summed HIP-event time on the launch stream (median over reps)."""
+    S, cp, H, G, d = w.total_tokens, w.cp, w.n_hq, w.n_kv, w.head_dim
+    cu = w.cu_seqlens
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, "cuda")
+    loc = []
+    for r in range(cp):
+        idx = torch.from_numpy(ca.balanced_split(cu, cp, r)[0]).to("cuda")
+        loc.append(tuple(t.index_select(0, idx).contiguous() for t in (q, k, v)))
+    del q, k, v
+    desc = ca.PrefillDesc(cp=cp, cu_seqlens=cu, n_hq=H, n_kv=G, head_dim=d, dtype=w.dtype, scale=w.softmax_scale)
+    rows = S // cp
+    acc = ca.new_partial(rows, H, d)
+    out = torch.empty(rows, H, d, device="cuda")
+    lse = torch.empty(rows, H, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)["rank_flops_exact"] * cp
+    totals = []
+    for rep_i in range(reps + 1):
+        evs = []
+        for r in range(cp):
+            for t in range(cp):
+                j = (r - t) % cp
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                ca.ring_step_partial(desc, r, t, loc[r][0], loc[j][1], loc[j][2], acc, accumulate=t > 0)
+                e1.record(stream)
+                evs.append((e0, e1))
+            ca.merge(acc, [], out=out, lse=lse)
+        torch.cuda.synchronize()
+        if rep_i:
+            totals.append(sum(a.elapsed_time(b) for a, b in evs))
+    ms = float(np.median(totals))
+    del loc
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "ring_ms": round(ms, 3), "launches": cp * cp, "flops": flops}
+
+
+def _decode_gbs(ca, torch, b, S, cp, H, G, d, reps=5):
+    n = S // cp
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    q = torch.randn(b, H, d, device="cuda", generator=gen).to(torch.bfloat16)
+    ks = [torch.randn(b, n, G, d, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(cp)]
+    vs = [torch.randn(b, n, G, d, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(cp)]
+    desc = ca.DecodeDesc(batch=b, cp=cp, kv_len=S, n_hq=H, n_kv=G, head_dim=d, dtype="bf16", scale=d ** -0.5)
+    sp = ca.new_partial(cp * b, H, d)
+    out = torch.empty(b, H, d, device="cuda")
+    lse = torch.empty(b, H, device="cuda")
+    ws = torch.empty(max(ca.passq_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ca.passq_decode(desc, q, ks, vs, sp, out, lse, ws=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    kv = 2 * b * S * G * d * 2
+    byts = kv + q.numel() * 2 + cp * b * H * (d + 2) * 4 + b * H * (d + 1) * 4
+    del ks, vs
+    return {"ms": round(ms, 3), "gb_per_s": round(byts / (ms * 1e-3) / 1e9, 1),
+            "frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": byts}
+
+
+def configs_report(ca, synth, torch):
+    """The other workloads, after the timed steps: the GQA prefill and the
+    wide-head varlen prefill as full rings over every rank, and the pass-Q decode
+    with one kv head (MQA 32/1 at head_dim 128; MLA-like 128/1 at head_dim 512;
+    b = 8, kv_len = 1048576, cp = 8, K/V ~ N(0,1))."""
+    log("bench: GQA prefill, full ring")
+    gqa = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS["gqa"])
+    torch.cuda.empty_cache()
+    log("bench: wide-head varlen prefill, full ring")
+    wide = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS["varlen"], reps=2)
+    torch.cuda.empty_cache()
+    log("bench: single-kv-head decode")
+    mqa = _decode_gbs(ca, torch, 8, 1 << 20, 8, 32, 1, 128)
+    torch.cuda.empty_cache()
+    mla = _decode_gbs(ca, torch, 8, 1 << 20, 8, 128, 1, 512)
+    torch.cuda.empty_cache()
+    return {
+        "gqa_prefill": dict(workload="S=32768, cp=8, 32q/8kv, d128, bf16; all 8 ranks x 8 steps", **gqa),
+        "wide_varlen_prefill": dict(workload=f"6 packed sequences ({synth.WORKLOADS['varlen'].total_tokens} tokens), "
+                                             "cp=4, 64 heads, d512, bf16; all 4 ranks x 4 steps", **wide),
+        "mqa_decode": dict(workload="b=8, kv_len=1048576, cp=8, 32q/1kv, d128, bf16", **mqa),
+        "mla_like_decode": dict(workload="b=8, kv_len=1048576, cp=8, 128q/1kv, d512, bf16", **mla),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the measurements of the other workloads that follow the timed steps")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the transfer/compute overlap measurements that follow the timed steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -293,6 +391,8 @@ def main():
         res["overlap"] = overlap_report(ca, synth, torch, pdesc, q0, blocks)
     del blocks
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        res["configs"] = configs_report(ca, synth, torch)
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
