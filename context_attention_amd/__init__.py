@@ -33,7 +33,7 @@ _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPP
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
 
-EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
+EXPORTS = ["cpattn_tree_reduce", "cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
            "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_passq_decode", "cpattn_account",
            "cpattn_version"]
 
@@ -106,6 +106,7 @@ def load():
                                                    ctypes.POINTER(_Partial), i32, vp, vp]
     lib.cpattn_merge.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, ctypes.POINTER(_Partial),
                                  vp, vp, vp]
+    lib.cpattn_tree_reduce.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, vp, vp, vp]
     lib.cpattn_passq_decode.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp,
                                         ctypes.POINTER(ctypes.c_size_t), vp]
@@ -357,6 +358,32 @@ def merge(acc: Partial, parts: Sequence[Partial] = (), out=None, lse=None, strea
     _check(lib.cpattn_merge(rows, n_hq, hd, arr if parts else None, len(parts), ctypes.byref(a),
                             out.data_ptr() if out is not None else None,
                             lse.data_ptr() if lse is not None else None, _stream(stream)), "cpattn_merge")
+
+
+def tree_reduce(parts: Sequence[Partial], out=None, lse=None, stream=None) -> None:
+    """cpattn_tree_reduce: merges `parts` in tree order (round k merges part
+    s + 2^k into part s, s a multiple of 2^(k+1)); parts[0] then holds the
+    result, the other parts are overwritten; optionally out = num/den, lse."""
+    lib = load()
+    if not parts:
+        raise ValueError("at least one part")
+    rows, n_hq, hd = parts[0].num.shape
+    for p in parts:
+        if p.num.shape != parts[0].num.shape or p.m.shape != parts[0].m.shape:
+            raise ValueError("part shape mismatch")
+    if out is not None:
+        _dev_check(out, "f32")
+        if tuple(out.shape) != (rows, n_hq, hd):
+            raise ValueError("out shape mismatch")
+    if lse is not None:
+        _dev_check(lse, "f32")
+        if tuple(lse.shape) != (rows, n_hq):
+            raise ValueError("lse shape mismatch")
+    arr = (_Partial * len(parts))(*[p._c() for p in parts])
+    _check(lib.cpattn_tree_reduce(rows, n_hq, hd, arr, len(parts),
+                                  out.data_ptr() if out is not None else None,
+                                  lse.data_ptr() if lse is not None else None, _stream(stream)),
+           "cpattn_tree_reduce")
 
 
 def passq_workspace_bytes(desc: DecodeDesc) -> int:

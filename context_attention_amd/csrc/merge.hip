@@ -119,3 +119,48 @@ extern "C" int cpattn_merge(int64_t rows, int32_t n_hq, int32_t head_dim, const 
   } while (done < n_parts);
   return CPATTN_OK;
 }
+
+// Tree-order reduction of n_parts triples (the Tree Attention reduction the
+// G5 spec lists as follow-up work for pass-Q: Limitations table, "pass-Q
+// reduction topology fixed"): round k merges part s + 2^k into part s for every
+// s that is a multiple of 2^(k+1), the exchange pattern of a tree over n_parts
+// ranks; ceil(log2 n_parts) rounds, n_parts - 1 merges in all. Each merge is one
+// merge_kernel launch with the receiving part as the accumulator.
+extern "C" int cpattn_tree_reduce(int64_t rows, int32_t n_hq, int32_t head_dim, const cpattn_partial *parts,
+                                  int32_t n_parts, float *out, float *lse, hipStream_t stream) {
+  using namespace cpattn;
+  if (rows < 0 || n_hq < 1 || n_parts < 1 || parts == nullptr) return CPATTN_E_ARG;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 512) return CPATTN_E_UNSUPPORTED;
+  for (int p = 0; p < n_parts; ++p) {
+    if (parts[p].m == nullptr || parts[p].den == nullptr || parts[p].num == nullptr) return CPATTN_E_ARG;
+    for (int q = 0; q < p; ++q)   // a part merged into itself would be counted twice
+      if (parts[p].m == parts[q].m || parts[p].den == parts[q].den || parts[p].num == parts[q].num)
+        return CPATTN_E_ARG;
+  }
+  if (rows == 0) return CPATTN_OK;
+  const int64_t items = rows * (int64_t)n_hq;
+  if ((items + 3) / 4 > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
+  auto launch = [&](const cpattn_partial *from, const cpattn_partial &into, float *o, float *l) {
+    MergeArgs a;
+    a.n_parts = from ? 1 : 0;
+    if (from) {
+      a.pm[0] = from->m;
+      a.pd[0] = from->den;
+      a.pn[0] = from->num;
+    }
+    a.am = into.m;
+    a.ad = into.den;
+    a.an = into.num;
+    a.out = o;
+    a.lse = l;
+    a.items = items;
+    if (head_dim == 64) return launch_merge<64>(a, stream);
+    if (head_dim == 128) return launch_merge<128>(a, stream);
+    return launch_merge<512>(a, stream);
+  };
+  for (int span = 1; span < n_parts; span *= 2)
+    for (int s = 0; s + span < n_parts; s += 2 * span)
+      if (launch(&parts[s + span], parts[s], nullptr, nullptr) != hipSuccess) return CPATTN_E_DEVICE;
+  if ((out != nullptr || lse != nullptr) && launch(nullptr, parts[0], out, lse) != hipSuccess) return CPATTN_E_DEVICE;
+  return CPATTN_OK;
+}

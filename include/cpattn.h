@@ -217,6 +217,23 @@ int cpattn_merge(int64_t rows, int32_t n_hq, int32_t head_dim,
                  const cpattn_partial *parts, int32_t n_parts, const cpattn_partial *acc,
                  float *out, float *lse, hipStream_t stream);
 
+/* Tree-order reduction of partial triples: the Tree Attention reduction that
+ * the spec lists as follow-up work for pass-Q (Limitations table, "pass-Q
+ * reduction topology fixed": its O(log) steps are not visible with a fixed
+ * topology). With one triple per rank, round k (k = 0, 1, ...) merges part
+ * s + 2^k into part s for every s that is a multiple of 2^(k+1): the exchanges
+ * of a tree over n_parts ranks, ceil(log2 n_parts) rounds and n_parts - 1
+ * merges. The merge is the associative one of cpattn_merge, so the result
+ * equals the linear reduction up to the order of fp32 rounding.
+ *   parts  HOST array of n_parts >= 1 device triples [rows, n_hq(, head_dim)],
+ *          pairwise distinct. Overwritten: after the call parts[0] holds the
+ *          merged triple, the others the partial results of the rounds.
+ *   out    device fp32 [rows, n_hq, head_dim] or NULL: num / den of the result.
+ *   lse    device fp32 [rows, n_hq] or NULL: m + ln(den).
+ * Errors: E_ARG (bad counts, null or repeated parts), E_UNSUPPORTED, E_DEVICE. */
+int cpattn_tree_reduce(int64_t rows, int32_t n_hq, int32_t head_dim, const cpattn_partial *parts,
+                       int32_t n_parts, float *out, float *lse, hipStream_t stream);
+
 /* Pass-Q decode (Definitions table, "Pass-Q"; Use case, decode): the query is
  * sent to every shard, shard s computes the partial triple over its kv_len/cp
  * keys (no mask), and the cp shard triples are reduced into the result.

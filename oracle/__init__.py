@@ -27,6 +27,8 @@ from .cp_oracle import (  # noqa: F401
     decode_reference,
     finalize,
     merge,
+    merge_tree,
+    tree_rounds,
     merge_two,
     partial_attention,
     passq_decode,

@@ -307,6 +307,31 @@ def merge(parts: Sequence[Triple]) -> Triple:
     return acc
 
 
+def tree_rounds(n: int) -> List[List[Tuple[int, int]]]:
+    """The exchanges of a tree reduction over n ranks, the Tree Attention
+    reduction that the G5 spec lists as follow-up work for pass-Q (Limitations
+    table): round k holds the pairs (receiver s, sender s + 2^k) for every s that
+    is a multiple of 2^(k+1) with s + 2^k < n."""
+    if n < 1:
+        raise ValueError("at least one rank")
+    rounds = []
+    span = 1
+    while span < n:
+        rounds.append([(s, s + span) for s in range(0, n - span, 2 * span)])
+        span *= 2
+    return rounds
+
+
+def merge_tree(parts: Sequence[Triple]) -> Triple:
+    """Merges one triple per rank along tree_rounds: after the last round rank 0
+    holds the result. `parts` is left untouched."""
+    held = list(parts)
+    for rnd in tree_rounds(len(held)):
+        for recv, send in rnd:
+            held[recv] = merge_two(held[recv], held[send])
+    return held[0]
+
+
 def finalize(t: Triple) -> Tuple[np.ndarray, np.ndarray]:
     """out = num / den, lse = m + ln(den); identity rows give out 0, lse -inf."""
     m, den, num = t

@@ -247,3 +247,21 @@ def test_padded_split_errors():
     with pytest.raises(ca.CpattnError) as e:
         ca.balanced_split_padded([0, 5], 2, 2)
     assert e.value.code == ca.E_ARG
+
+
+def test_tree_reduce_rejects_bad_arguments_without_gpu():
+    """cpattn_tree_reduce validates counts, pointers and repeated parts before
+    any launch; rows = 0 is a no-op."""
+    lib = ca.load()
+    P = ca._Partial
+    a, b = P(4096, 8192, 16384), P(32768, 65536, 131072)
+    arr = (P * 2)(a, b)
+    assert lib.cpattn_tree_reduce(4, 2, 128, None, 2, None, None, None) == ca.E_ARG
+    assert lib.cpattn_tree_reduce(4, 2, 128, arr, 0, None, None, None) == ca.E_ARG
+    assert lib.cpattn_tree_reduce(-1, 2, 128, arr, 2, None, None, None) == ca.E_ARG
+    assert lib.cpattn_tree_reduce(4, 2, 96, arr, 2, None, None, None) == ca.E_UNSUPPORTED
+    same = (P * 2)(a, a)
+    assert lib.cpattn_tree_reduce(4, 2, 128, same, 2, None, None, None) == ca.E_ARG
+    nul = (P * 2)(a, P(0, 65536, 131072))
+    assert lib.cpattn_tree_reduce(4, 2, 128, nul, 2, None, None, None) == ca.E_ARG
+    assert lib.cpattn_tree_reduce(0, 2, 128, arr, 2, None, None, None) == ca.OK

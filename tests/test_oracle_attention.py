@@ -227,3 +227,52 @@ def test_decode_brute_force():
         np.broadcast_to(q[0], (S, hq, d)), k[0], v[0], [0, S], 0.5, causal=False)
     np.testing.assert_allclose(o[0], bo[0], atol=1e-13)
     np.testing.assert_allclose(l[0], bl[0], atol=1e-13)
+
+
+def test_tree_rounds_hand_worked():
+    """The tree's exchanges, worked by hand from its definition (round k: rank
+    s + 2^k sends to rank s for s a multiple of 2^(k+1))."""
+    assert oracle.tree_rounds(1) == []
+    assert oracle.tree_rounds(2) == [[(0, 1)]]
+    assert oracle.tree_rounds(3) == [[(0, 1)], [(0, 2)]]
+    assert oracle.tree_rounds(5) == [[(0, 1), (2, 3)], [(0, 2)], [(0, 4)]]
+    assert oracle.tree_rounds(8) == [[(0, 1), (2, 3), (4, 5), (6, 7)], [(0, 2), (4, 6)], [(0, 4)]]
+
+
+@pytest.mark.parametrize("n", list(range(1, 18)))
+def test_tree_rounds_structure(n):
+    """ceil(log2 n) rounds and n - 1 exchanges; every rank but 0 sends exactly
+    once and receives nothing after it has sent; in each round a rank takes part
+    in at most one exchange."""
+    rounds = oracle.tree_rounds(n)
+    assert len(rounds) == (n - 1).bit_length()
+    sent = set()
+    for rnd in rounds:
+        busy = set()
+        for recv, send in rnd:
+            assert recv not in sent and send not in sent
+            assert recv not in busy and send not in busy
+            busy |= {recv, send}
+        sent |= {send for _, send in rnd}
+    assert sent == set(range(1, n))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 9])
+def test_merge_tree_equals_linear_merge(n):
+    """The tree merge gives the linear merge's triple (associativity), on
+    triples with very different maxima, identity triples among them."""
+    rng = np.random.default_rng(60 + n)
+    parts = []
+    for i in range(n):
+        m = rng.normal(size=(3, 2)) * 20
+        den = rng.uniform(0.5, 4, size=(3, 2))
+        num = rng.normal(size=(3, 2, 4))
+        if i % 4 == 3:
+            m, den, num = np.full((3, 2), -np.inf), np.zeros((3, 2)), np.zeros((3, 2, 4))
+        parts.append((m, den, num))
+    t = oracle.merge_tree(parts)
+    lin = oracle.merge(parts)
+    o1, l1 = oracle.finalize(t)
+    o2, l2 = oracle.finalize(lin)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
