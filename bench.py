@@ -67,9 +67,11 @@ def cpu_baseline_prefill(w, rows=64, target_s=15.0):
         dt = time.perf_counter() - t0
     flops = 4 * d * H * rows * n
     cores = len(os.sched_getaffinity(0))
+    step_flops = 4 * d * H * c * n   # one ring step of rank 0 at t >= 1: its c tail-chunk rows see every key of the block
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} tail-chunk query rows of rank 0 x {H} heads against rank 7's full KV block "
                       f"({n} keys, ring step 1, no mask): {flops:.3e} flop in {dt:.2f} s (fp64 numpy)",
+            "extrapolated_step_s": round(step_flops / (flops / dt), 1),
             "seconds": dt}
 
 
@@ -152,7 +154,8 @@ def _full_ring_tflops(ca, synth, torch, w, reps=3):
     lse = torch.empty(rows, H, device="cuda")
     stream = torch.cuda.current_stream()
     flops = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)["rank_flops_exact"] * cp
-    totals = []
+    exact = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)
+    totals, per_call = [], []
     for rep_i in range(reps + 1):
         evs = []
         for r in range(cp):
@@ -166,11 +169,18 @@ def _full_ring_tflops(ca, synth, torch, w, reps=3):
             ca.merge(acc, [], out=out, lse=lse)
         torch.cuda.synchronize()
         if rep_i:
-            totals.append(sum(a.elapsed_time(b) for a, b in evs))
+            times = [a.elapsed_time(b) for a, b in evs]
+            totals.append(sum(times))
+            # per (rank, step): exact FLOPs of the call (step 0 holds the diagonal triangles)
+            per_call.append([(exact["step0_flops_exact"] if i % cp == 0 else exact["stepN_flops_exact"]) / (x * 1e-3) / 1e12
+                             for i, x in enumerate(times)])
     ms = float(np.median(totals))
+    calls = np.median(np.array(per_call), axis=0)
     del loc
     return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "ring_ms": round(ms, 3), "launches": cp * cp, "flops": flops}
+            "ring_ms": round(ms, 3), "launches": cp * cp, "flops": flops,
+            "per_call_tflops": {"min": round(float(calls.min()), 1), "median": round(float(np.median(calls)), 1),
+                                "max": round(float(calls.max()), 1)}}
 
 
 def _decode_gbs(ca, torch, b, S, cp, H, G, d, reps=5):
