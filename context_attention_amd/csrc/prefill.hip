@@ -93,7 +93,7 @@ struct Cfg<128> {
 };
 template <>
 struct Cfg<512> {
-  static constexpr int BN = 32, NW = 8, NB = 1, WPE = 2;
+  static constexpr int BN = 32, NW = 8, WPE = 2;
   static constexpr int NS = 4;   // waves that share a 32-row block, each owning D / NS columns
 };
 template <int D>
