@@ -1,5 +1,5 @@
-// Host-only entry points of cpattn: the balanced chunk split and the
-// byte / FLOP / memory account. Plain C++ with no GPU code, so it builds with
+// Host-only entry points of cpattn: the balanced chunk split (and its padded
+// form for lengths not divisible by 2*cp) and the byte / FLOP / memory account. Plain C++ with no GPU code, so it builds with
 // g++ as well as with hipcc.
 #include "cpattn.h"
 
@@ -150,4 +150,4 @@ extern "C" int cpattn_account(const cpattn_account_in *in, cpattn_account_out *o
   return CPATTN_OK;
 }
 
-extern "C" const char *cpattn_version(void) { return "cpattn 0.1.0 gfx950"; }
+extern "C" const char *cpattn_version(void) { return "cpattn 0.2.0 gfx950"; }

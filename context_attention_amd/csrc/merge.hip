@@ -6,7 +6,8 @@
 // One wavefront per (row, head): every lane reads the n_parts + 1 maxima and
 // denominators (the same addresses, served as broadcasts), computes the merge
 // weights, rescales and sums its share of the numerator, and lane 0 writes
-// back the merged max and denominator after all lanes have read them.
+// back the merged max and denominator after all lanes have read them. The
+// tree-order reduction at the end of this file chains the same kernel.
 #include "kernels.h"
 
 namespace cpattn {

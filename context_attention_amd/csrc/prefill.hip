@@ -7,18 +7,20 @@
 // a_t = 2cp-1-r (tail) of every sequence; the block of rank j holds key chunks
 // b_h = j and b_t = 2cp-1-j. A (query chunk a, key chunk b) pair of the same
 // sequence is fully visible when b < a, a causal triangle when b == a (only at
-// step 0) and empty when b > a. Both kernels below walk, for their query rows,
+// step 0) and empty when b > a. The kernels below walk, for their query rows,
 // only the key chunks that are not empty, and mask only the triangle and the
-// ragged end of a chunk.
+// ragged end of a chunk. In the padded layout (lengths rounded up to a multiple
+// of 2cp) a chunk's real tokens are its first min(c, L - chunk c) slots: key
+// segments stop there and rows past it get the merge identity.
 //
 // Kernels
 //   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 8 waves (two per
 //       SIMD) owns 32*8/HG query rows x HG query heads of one kv group; K and V
 //       tiles of 64 keys are copied straight from HBM into double-buffered LDS
 //       (the next tiles' copies are in flight while the current one computes)
-//       and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_32x32x16_bf16, so
-//       every lane owns one query column of both products and the softmax needs a
-//       single cross-lane exchange per tile.
+//       and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on
+//       v_mfma_f32_32x32x16_bf16, so every lane owns one query column of both
+//       products and the softmax needs a single cross-lane exchange per tile.
 //   ring_step_wide<HG>  bf16, head_dim 512: wave quads split d (below).
 //   ring_step_generic<T, D>  fp32: one workgroup per (query row, query head),
 //       fp32 arithmetic throughout.

@@ -7,7 +7,12 @@
  * triple (max, numerator, denominator), the associative merge of triples,
  * pass-Q decode (per-shard partials plus the reduction of the three
  * quantities), and the byte / FLOP / memory formulas of its Formulas section.
- * Sections cited below are sections of that page.
+ * Around them: the one-GPU emulation of the ring's block transfers overlapped
+ * with its compute (the spec's dependency contract), a padded layout for
+ * sequence lengths not divisible by 2*cp (after the padding rule of the TP/EP
+ * design page), and a tree-order reduction of triples (the spec's follow-up
+ * work). Sections cited below are sections of the G5 spec unless another page
+ * is named.
  *
  * Conventions shared by every entry point
  *   - Return value: CPATTN_OK (0) or one of the CPATTN_E_* codes. Nothing is
@@ -142,11 +147,13 @@ int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t num_seqs, in
  * rank (rank - step) mod cp holds:
  *   visible keys: same sequence, global key position <= global query position;
  *   triple over them as in cpattn_partial (rows that see no key: identity).
- *   q_local  device [S/cp, n_hq, head_dim] rows of `rank`, in the local order of
- *            cpattn_balanced_split (S = cu_seqlens[num_seqs]).
- *   k_blk, v_blk  device [S/cp, n_kv, head_dim], the rows of rank (rank-step) mod cp
+ *   q_local  device [R, n_hq, head_dim] rows of `rank`, in the local order of
+ *            cpattn_balanced_split (or cpattn_balanced_split_padded when
+ *            desc->padded). R = S/cp with S = cu_seqlens[num_seqs]; padded:
+ *            R = sum over sequences of 2 * ceil(L_i / (2 cp)).
+ *   k_blk, v_blk  device [R, n_kv, head_dim], the rows of rank (rank-step) mod cp
  *            in that rank's local order.
- *   dst      device triple for S/cp rows.
+ *   dst      device triple for R rows.
  *   accumulate  0: dst = partial; 1: dst = merge(dst, partial) (dst must then hold
  *            a valid triple, e.g. the previous step's result).
  * bf16 inputs use MFMA with fp32 accumulation; fp32 inputs compute in fp32.
