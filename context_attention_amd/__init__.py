@@ -7,7 +7,7 @@ is no fallback path.
 
 Entry points mirror the C names of include/cpattn.h:
     balanced_split, balanced_split_padded, ring_step_partial, ring_pass, ring_prefill_overlapped,
-    merge, passq_decode, account
+    merge, tree_reduce, passq_decode, account
 """
 from __future__ import annotations
 
@@ -20,8 +20,8 @@ import numpy as np
 
 __all__ = [
     "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
-    "balanced_split", "balanced_split_padded", "ring_step_partial", "ring_pass", "ring_prefill_overlapped", "merge",
-    "passq_decode", "passq_workspace_bytes",
+    "balanced_split", "balanced_split_padded", "padded_rows", "ring_step_partial", "ring_pass",
+    "ring_prefill_overlapped", "merge", "tree_reduce", "passq_decode", "passq_workspace_bytes",
     "account", "new_partial",
 ]
 
@@ -33,9 +33,9 @@ _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPP
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
 
-EXPORTS = ["cpattn_tree_reduce", "cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
-           "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_passq_decode", "cpattn_account",
-           "cpattn_version"]
+EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
+           "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_tree_reduce", "cpattn_passq_decode",
+           "cpattn_account", "cpattn_version"]
 
 
 class CpattnError(RuntimeError):
