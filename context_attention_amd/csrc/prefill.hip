@@ -358,6 +358,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
   f32x16_t snext[NB][MB];
   qk_tile<D, NB>(Ks[0], qf, snext);
+  // copy descriptors of the next iteration, computed one iteration ahead
+  u32x4_t kd = tile_at(kblock, 2), vd = tile_at(vblock, 1);
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -368,8 +370,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
     // prefetch: K of tile it+2 into the LDS buffer of K of tile it (read in the
     // previous iteration) and V of tile it+1 into that of V of tile it-1
-    load_tile<D>(smap.k, tile_at(kblock, it + 2), Ks[cur]);
-    load_tile<D>(smap.v, tile_at(vblock, it + 1), Vt[cur ^ 1]);
+    load_tile<D>(smap.k, kd, Ks[cur]);
+    load_tile<D>(smap.v, vd, Vt[cur ^ 1]);
 
     f32x16_t sacc[NB][MB];
 #pragma unroll
@@ -458,6 +460,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       }
     }
 
+    kd = tile_at(kblock, it + 3);
+    vd = tile_at(vblock, it + 2);
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -643,6 +647,8 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   qk_half(Ks[0], spart);
   put_scores(Sx[wave], spart);
   __syncthreads();
+  // copy descriptors of the next iteration, computed one iteration ahead
+  u32x4_t kd = tile_at(kblock, 2), vd = tile_at(vblock, 1);
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -651,8 +657,8 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    load_tile<D>(smap.k, tile_at(kblock, it + 2), Ks[cur]);
-    load_tile<D>(smap.v, tile_at(vblock, it + 1), Vt[cur ^ 1]);
+    load_tile<D>(smap.k, kd, Ks[cur]);
+    load_tile<D>(smap.v, vd, Vt[cur ^ 1]);
 
     // full scores of tile it: the group's partials summed in one fixed order
     f32x16_t sacc = get_scores(Sx[grp * NS]);
@@ -707,6 +713,8 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       }
     }
 
+    kd = tile_at(kblock, it + 3);
+    vd = tile_at(vblock, it + 2);
     put_scores(Sx[wave], spart);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
