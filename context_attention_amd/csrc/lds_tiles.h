@@ -40,7 +40,7 @@ constexpr int kWaitLgkm0 = 0xC07F;               // s_waitcnt lgkmcnt(0)
 
 // Buffer resource of a tile: base at key row `row`, loads at or past
 // rows_left * row_bytes return zeros.
-__device__ __forceinline__ u32x4_t tile_words(const char *block, int64_t row, int rows_left, uint32_t row_bytes) {
+__host__ __device__ __forceinline__ u32x4_t tile_words(const char *block, int64_t row, int rows_left, uint32_t row_bytes) {
   const int64_t lim = (int64_t)rows_left * row_bytes;
   const uint32_t nrec = (uint32_t)(lim < 0x7FFFFFFF ? lim : 0x7FFFFFFF);
   const uint64_t base = (uint64_t)(block + row * (int64_t)row_bytes);

@@ -57,11 +57,12 @@ struct StepArgs {
 
 // Real (non-pad) tokens of chunk `chunk` of a sequence of true length len
 // split into chunks of c slots.
-__device__ __forceinline__ int chunk_valid(int len, int chunk, int c) {
-  return max(0, min(c, len - chunk * c));
+__host__ __device__ __forceinline__ int chunk_valid(int len, int chunk, int c) {
+  const int v = len - chunk * c;
+  return v < 0 ? 0 : (v < c ? v : c);
 }
 
-__device__ __forceinline__ int find_seq(const SeqTable &t, int32_t unit) {
+__host__ __device__ __forceinline__ int find_seq(const SeqTable &t, int32_t unit) {
   int i = 0;
   while (i + 1 < t.n && t.start[i + 1] <= unit) ++i;
   return i;
@@ -191,9 +192,9 @@ struct Segs {
   int64_t row[2];         // first key row of each segment in the block
   int end[2];             // visible keys of each segment
   bool diag[2];
-  __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
-  __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * BN; }
-  __device__ __forceinline__ int tiles() const {
+  __host__ __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
+  __host__ __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * BN; }
+  __host__ __device__ __forceinline__ int tiles() const {
     return n0 + (nseg > 1 ? (end[1] + BN - 1) / BN : 0);
   }
 };
@@ -203,11 +204,13 @@ struct Segs {
 // and holds a real key. A diagonal segment (same chunk) ends at the
 // workgroup's last real row; others at the chunk's real keys.
 template <int BN>
-__device__ __forceinline__ Segs<BN> make_segs(const StepArgs &a, int qa, int c, int len, int64_t row_off,
+__host__ __device__ __forceinline__ Segs<BN> make_segs(const StepArgs &a, int qa, int c, int len, int64_t row_off,
                                               int row_end) {
   const bool diag_t = a.b_tail == qa, diag_h = a.b_head == qa;
-  const int end_t = min(diag_t ? row_end : c, chunk_valid(len, a.b_tail, c));
-  const int end_h = min(diag_h ? row_end : c, chunk_valid(len, a.b_head, c));
+  const int lim_t = diag_t ? row_end : c, lim_h = diag_h ? row_end : c;
+  const int val_t = chunk_valid(len, a.b_tail, c), val_h = chunk_valid(len, a.b_head, c);
+  const int end_t = lim_t < val_t ? lim_t : val_t;
+  const int end_h = lim_h < val_h ? lim_h : val_h;
   const bool ok_t = a.b_tail <= qa && end_t > 0;
   const bool ok_h = a.b_head <= qa && end_h > 0;
   Segs<BN> sg;
@@ -221,6 +224,63 @@ __device__ __forceinline__ Segs<BN> make_segs(const StepArgs &a, int qa, int c, 
   sg.n0 = (sg.end[0] + BN - 1) / BN;
   return sg;
 }
+
+// Buffer resource of tile t of the key segments: based at the tile's first key
+// row, with the visible keys of its segment from there on as the range; past
+// the last tile an empty range at the block start (the copy then writes zeros
+// and touches no memory, so the tile loops need no branch).
+template <int BN>
+__host__ __device__ __forceinline__ u32x4_t seg_tile_words(const Segs<BN> &sg, int ntiles, const char *blk, int t,
+                                                           uint32_t rb) {
+  const bool ok = t < ntiles;
+  const int s = sg.seg(t), k = sg.k0(t);
+  return tile_words(blk, ok ? sg.row[s] + k : 0, ok ? sg.end[s] - k : 0, rb);
+}
+
+// seg_tile_words for the tiles t0, t0 + 1, ... as running sums: each step moves
+// the tile's address forward and its range down by one tile, and the second
+// segment's first tile restarts both from that segment, so a step costs a few
+// scalar additions instead of the products and selects. The resources are the
+// same words bit for bit (the range clamp is done on the two 32-bit halves).
+template <int BN>
+struct TileWalk {
+  int t, n0, ntiles;
+  uint64_t blk;
+  uint64_t addr;          // address of tile t's first key row
+  int64_t lim;            // bytes of visible keys from there to its segment's end
+  uint64_t addr1;         // the same for the first tile of the second segment
+  int64_t lim1;
+  int64_t step;           // bytes of one tile
+  __host__ __device__ __forceinline__ TileWalk(const Segs<BN> &sg, int ntiles_, const char *blk_, int t0,
+                                               uint32_t rb)
+      : t(t0), n0(sg.n0), ntiles(ntiles_), blk((uint64_t)(uintptr_t)blk_) {
+    const int s = sg.seg(t0), k = sg.k0(t0);
+    addr = blk + (uint64_t)((sg.row[s] + k) * (int64_t)rb);
+    lim = (int64_t)(sg.end[s] - k) * rb;
+    addr1 = blk + (uint64_t)(sg.row[1] * (int64_t)rb);
+    lim1 = (int64_t)sg.end[1] * rb;
+    step = (int64_t)BN * rb;
+  }
+  __host__ __device__ __forceinline__ void next() {
+    ++t;
+    if (t == n0) {
+      addr = addr1;
+      lim = lim1;
+    } else {
+      addr += (uint64_t)step;
+      lim -= step;
+    }
+  }
+  // a tile before the end has lim > 0, so the clamp of tile_words to 0x7FFFFFFF
+  // reads as: high half zero and low half below the cap, else the cap
+  __host__ __device__ __forceinline__ u32x4_t words() const {
+    const bool ok = t < ntiles;
+    const uint64_t base = ok ? addr : blk;
+    const uint32_t lo = (uint32_t)(uint64_t)lim, hi = (uint32_t)((uint64_t)lim >> 32);
+    const uint32_t nrec = ok ? ((hi == 0u && lo < 0x7FFFFFFFu) ? lo : 0x7FFFFFFFu) : 0u;
+    return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, kBufferWord3};
+  }
+};
 
 template <int D, int HG>
 __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
@@ -348,18 +408,13 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  // buffer resource of tile t, or an empty range (the copy then writes zeros and
-  // touches no memory) past the last tile, so the loop body has no branch
-  auto tile_at = [&](const char *blk, int t) {
-    const bool ok = t < ntiles;
-    const int s = sg.seg(t), k = sg.k0(t);
-    return tile_words(blk, ok ? sg.row[s] + k : 0, ok ? sg.end[s] - k : 0, row_bytes);
-  };
 
   f32x16_t snext[NB][MB];
   qk_tile<D, NB>(Ks[0], qf, snext);
-  // copy descriptors of the next iteration, computed one iteration ahead
-  u32x4_t kd = tile_at(kblock, 2), vd = tile_at(vblock, 1);
+  // copy resources of K from tile 2 on and of V from tile 1 on; each iteration
+  // uses the pair computed at the end of the one before
+  TileWalk<BN> kw(sg, ntiles, kblock, 2, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
+  u32x4_t kd = kw.words(), vd = vw.words();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -460,8 +515,10 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
       }
     }
 
-    kd = tile_at(kblock, it + 3);
-    vd = tile_at(vblock, it + 2);
+    kw.next();
+    vw.next();
+    kd = kw.words();
+    vd = vw.words();
     // K of tile it+2 replaces K of tile it; V of tile it+1 replaces V of tile it-1
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -636,19 +693,14 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  // buffer resource of tile t, or an empty range (the copy then writes zeros and
-  // touches no memory) past the last tile, so the loop body has no branch
-  auto tile_at = [&](const char *blk, int t) {
-    const bool ok = t < ntiles;
-    const int s = sg.seg(t), k = sg.k0(t);
-    return tile_words(blk, ok ? sg.row[s] + k : 0, ok ? sg.end[s] - k : 0, row_bytes);
-  };
   f32x16_t spart;
   qk_half(Ks[0], spart);
   put_scores(Sx[wave], spart);
   __syncthreads();
-  // copy descriptors of the next iteration, computed one iteration ahead
-  u32x4_t kd = tile_at(kblock, 2), vd = tile_at(vblock, 1);
+  // copy resources of K from tile 2 on and of V from tile 1 on; each iteration
+  // uses the pair computed at the end of the one before
+  TileWalk<BN> kw(sg, ntiles, kblock, 2, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
+  u32x4_t kd = kw.words(), vd = vw.words();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
@@ -713,8 +765,10 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       }
     }
 
-    kd = tile_at(kblock, it + 3);
-    vd = tile_at(vblock, it + 2);
+    kw.next();
+    vw.next();
+    kd = kw.words();
+    vd = vw.words();
     put_scores(Sx[wave], spart);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
