@@ -169,12 +169,13 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[N
                                         f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, hf = lane >> 5;
+  // k-step major: consecutive products go to different accumulators
 #pragma unroll
-  for (int mb = 0; mb < Cfg<D>::BN / 32; ++mb) {
-    const int key = mb * 32 + qi;
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int ch = ks * 2 + hf;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int ch = ks * 2 + hf;
+    for (int mb = 0; mb < Cfg<D>::BN / 32; ++mb) {
+      const int key = mb * 32 + qi;
       const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -411,6 +412,8 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
   f32x16_t snext[NB][MB];
   qk_tile<D, NB>(Ks[0], qf, snext);
+  // every wave has read K of tile 0 before the first iteration's copy replaces it
+  __syncthreads();
   // copy resources of K from tile 2 on and of V from tile 1 on; each iteration
   // uses the pair computed at the end of the one before
   TileWalk<BN> kw(sg, ntiles, kblock, 2, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
@@ -451,12 +454,13 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     bool grows = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float x = kNegInf;
+      // four independent partial maxima, then combined
+      float x4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[nb][mb][r]);
-      mx[nb] = max_across_halves(x);
+        for (int r = 0; r < 16; ++r) x4[r & 3] = fmaxf(x4[r & 3], sacc[nb][mb][r]);
+      mx[nb] = max_across_halves(fmaxf(fmaxf(x4[0], x4[1]), fmaxf(x4[2], x4[3])));
       grows |= mx[nb] > m_ref[nb] + thr;
     }
     if (__any(grows)) {
