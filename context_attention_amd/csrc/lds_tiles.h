@@ -60,12 +60,15 @@ __device__ __forceinline__ u32x4_t uniform_words(u32x4_t r) {
 // compiler tracks its own buffer-to-LDS copies and, unable to tell LDS ranges
 // apart, makes the first LDS read after one wait for every outstanding vector
 // load, which would expose the whole load latency at the top of each tile. The
-// kernels wait for these copies themselves (s_waitcnt vmcnt).
+// kernels wait for these copies themselves (s_waitcnt vmcnt). gfx9 asks for one
+// wait state between a scalar write of M0 and an LDS DMA that reads it; the
+// compiler inserts it for its own copies but cannot see that this one reads M0
+// that way, so the s_nop is part of the copy.
 __device__ __forceinline__ void dma_1k(uint32_t off, u32x4_t rs, __bf16 *chunk) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16 *)chunk);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(lds));
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(lds));
 #else
   (void)off; (void)rs; (void)chunk;
 #endif
