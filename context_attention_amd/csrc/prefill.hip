@@ -164,9 +164,10 @@ __device__ __forceinline__ void unit_and_group(int n_hg, int &unit, int &hg) {
 
 // S^T = K Q^T for the keys of a staged tile, in 32-key blocks, for the NB
 // 32-row blocks of the wave: every K fragment read from LDS feeds NB MFMAs.
-template <int D, int NB>
+// `after(ks)` runs after each k-step (the ring step issues its copies there).
+template <int D, int NB, typename Hook>
 __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[NB][D / 16],
-                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
+                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32], Hook after) {
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, hf = lane >> 5;
   // k-step major: consecutive products go to different accumulators
@@ -182,7 +183,13 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[N
         sacc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], ks == 0 ? f32x16_t{} : sacc[nb][mb],
                                                               0, 0, 0);
     }
+    after(ks);
   }
+}
+template <int D, int NB>
+__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[NB][D / 16],
+                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
+  qk_tile<D, NB>(Kc, qf, sacc, [](int) {});
 }
 
 // Tile geometry of flattened tile index t over the (up to two) key segments.
@@ -427,9 +434,20 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     const bool diag = sg.diag[sc];
 
     // prefetch: K of tile it+2 into the LDS buffer of K of tile it (read in the
-    // previous iteration) and V of tile it+1 into that of V of tile it-1
-    load_tile<D>(smap.k, kd, Ks[cur]);
-    load_tile<D>(smap.v, vd, Vt[cur ^ 1]);
+    // previous iteration) and V of tile it+1 into that of V of tile it-1. The
+    // copies are spread over the k-steps of the next tile's QK^T rather than
+    // issued together: eight waves issuing them at once queue on the CU's load
+    // path (about 62 bytes per clock) with nothing else to run.
+    constexpr int KN = StageMap<D>::KN;
+    const u32x4_t rk = uniform_words(kd), rv = uniform_words(vd);
+    auto copy_after = [&](int ks) {
+#pragma unroll
+      for (int j = 0; j < 2 * KN; ++j)
+        if (j * KS / (2 * KN) == ks) {
+          if (j < KN) dma_1k(smap.k[j], rk, Ks[cur] + (wave * KN + j) * 512);
+          else dma_1k(smap.v[j - KN], rv, Vt[cur ^ 1] + (wave * KN + j - KN) * 512);
+        }
+    };
 
     f32x16_t sacc[NB][MB];
 #pragma unroll
@@ -484,7 +502,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
     // ---- one scheduling region: QK^T of the next tile (matrix cores) with this
     // tile's exponentials (vector ALUs), then this tile's PV product
-    qk_tile<D, NB>(Ks[cur ^ 1], qf, snext);
+    qk_tile<D, NB>(Ks[cur ^ 1], qf, snext, copy_after);
     uint32_t pk[NB][MB][8];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
