@@ -17,8 +17,9 @@
 //   ring_step_mfma<D, HG>  bf16, head_dim 64/128: a workgroup of 8 waves (two per
 //       SIMD) owns 32*8/HG query rows x HG query heads of one kv group; K and V
 //       tiles of 64 keys are copied straight from HBM into double-buffered LDS
-//       (the next tiles' copies are in flight while the current one computes)
-//       and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on
+//       (the next tiles' copies are in flight while the current one computes,
+//       issued between the k-steps of a QK^T, their buffer resources walked by
+//       running sums) and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on
 //       v_mfma_f32_32x32x16_bf16, so every lane owns one query column of both
 //       products and the softmax needs a single cross-lane exchange per tile.
 //   ring_step_wide<HG>  bf16, head_dim 512: wave quads split d (below).
