@@ -1044,6 +1044,8 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
   const int G = d.n_hq / d.n_kv;
   if (!(G == 1 || G == 2 || G == 4 || G % 8 == 0)) return CPATTN_E_UNSUPPORTED;
   if (d.cp > kMaxShards) return CPATTN_E_UNSUPPORTED;
+  // a tile's key rows lie within the 2^31-byte range of one copy resource
+  if ((int64_t)d.n_kv * d.head_dim * 2 * 64 > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
 
   const DecodePlan p = plan_decode(d);
   const int32_t nsplit = p.nsplit;

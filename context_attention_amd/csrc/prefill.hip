@@ -69,8 +69,8 @@ __host__ __device__ __forceinline__ int find_seq(const SeqTable &t, int32_t unit
   return i;
 }
 
-// Writes one (row, head) triple; with accumulate, merges into what is there.
-// `num_vals` are this thread's elements at d indices given by the caller.
+// Stores the max and the denominator of one (row, head) triple (the caller
+// stores the numerator and has already merged with the old triple if asked).
 __device__ __forceinline__ void store_stats(float *mp, float *dp, float m_new, float d_new) {
   *mp = m_new;
   *dp = d_new;
@@ -1041,6 +1041,8 @@ int cpattn::check_prefill(const cpattn_prefill_desc *desc, int32_t rank, int32_t
   const int d = desc->head_dim;
   if (d != 64 && d != 128 && d != 512) return CPATTN_E_UNSUPPORTED;
   if (desc->n_hq > 65535) return CPATTN_E_UNSUPPORTED;
+  // the 64 key rows of a tile lie within the 2^31-byte range of one copy resource
+  if ((int64_t)desc->n_kv * d * 2 * 64 > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
   if (desc->padded != 0 && desc->padded != 1) return CPATTN_E_ARG;
   const int64_t *cu = desc->cu_seqlens;
   if (desc->num_seqs > 0 && cu[0] != 0) return CPATTN_E_ARG;

@@ -157,7 +157,9 @@ int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t num_seqs, in
  *   accumulate  0: dst = partial; 1: dst = merge(dst, partial) (dst must then hold
  *            a valid triple, e.g. the previous step's result).
  * bf16 inputs use MFMA with fp32 accumulation; fp32 inputs compute in fp32.
- * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_DEVICE. */
+ * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED (head_dim not 64/128/512,
+ * n_hq > 65535, a length > 2^30, or n_kv * head_dim >= 2^24, where 64 key rows
+ * pass 2^31 bytes), E_DEVICE. */
 int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int32_t step,
                              const void *q_local, const void *k_blk, const void *v_blk,
                              const cpattn_partial *dst, int32_t accumulate, hipStream_t stream);
@@ -255,7 +257,8 @@ int cpattn_tree_reduce(int64_t rows, int32_t n_hq, int32_t head_dim, const cpatt
  *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the
  *             required size in *ws_bytes and returns CPATTN_OK. Otherwise *ws_bytes
  *             is the size available (E_WORKSPACE if too small).
- * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_WORKSPACE, E_DEVICE. */
+ * Errors: E_ARG, E_DIVISIBILITY, E_UNSUPPORTED (also cp > 64 shards, or
+ * n_kv * head_dim >= 2^24), E_WORKSPACE, E_DEVICE. */
 int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q,
                         const void *const *k_shards, const void *const *v_shards,
                         const cpattn_partial *shard_partials, float *out, float *lse,

@@ -138,6 +138,8 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
         (desc(dtype=7), 0, 0, ca.E_ARG),
         (desc(scale=0.0), 0, 0, ca.E_ARG),
         (desc(scale=float("nan")), 0, 0, ca.E_ARG),
+        # 64 key rows of n_kv * head_dim bf16 values past 2^31 bytes
+        (desc(n_hq=32768, n_kv=32768, head_dim=512), 0, 0, ca.E_UNSUPPORTED),
     ]
     cu_bad = np.array([0, 10], dtype=np.int64)
     cases.append((desc(cu_seqlens=cu_bad.ctypes.data_as(P)), 0, 0, ca.E_DIVISIBILITY))
@@ -166,6 +168,10 @@ def test_device_entry_points_reject_bad_arguments_without_gpu():
     bad = ca._DecodeDesc(batch=8, cp=8, kv_len=1 << 20, n_hq=24, n_kv=8, head_dim=128, dtype=ca.DT_BF16,
                          scale=0.1)
     assert lib.cpattn_passq_decode(ctypes.byref(bad), None, None, None, None, None, None, None,
+                                   ctypes.byref(n), None) == ca.E_UNSUPPORTED
+    big = ca._DecodeDesc(batch=1, cp=1, kv_len=64, n_hq=32768, n_kv=32768, head_dim=512, dtype=ca.DT_BF16,
+                         scale=0.1)
+    assert lib.cpattn_passq_decode(ctypes.byref(big), None, None, None, None, None, None, None,
                                    ctypes.byref(n), None) == ca.E_UNSUPPORTED
     # query heads per kv head: 1, 2, 4 or a multiple of 8 (MQA-like groups included)
     for n_hq, n_kv, code in ((48, 8, ca.E_UNSUPPORTED), (12, 1, ca.E_UNSUPPORTED), (16, 1, ca.OK),
