@@ -165,10 +165,9 @@ __device__ __forceinline__ void unit_and_group(int n_hg, int &unit, int &hg) {
 
 // S^T = K Q^T for the keys of a staged tile, in 32-key blocks, for the NB
 // 32-row blocks of the wave: every K fragment read from LDS feeds NB MFMAs.
-// `after(ks)` runs after each k-step (the ring step issues its copies there).
-template <int D, int NB, typename Hook>
+template <int D, int NB>
 __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[NB][D / 16],
-                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32], Hook after) {
+                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
   const int lane = threadIdx.x & 63;
   const int qi = lane & 31, hf = lane >> 5;
   // k-step major: consecutive products go to different accumulators
@@ -184,13 +183,7 @@ __device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[N
         sacc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], ks == 0 ? f32x16_t{} : sacc[nb][mb],
                                                               0, 0, 0);
     }
-    after(ks);
   }
-}
-template <int D, int NB>
-__device__ __forceinline__ void qk_tile(const __bf16 *Kc, const bf16x8_t (&qf)[NB][D / 16],
-                                        f32x16_t (&sacc)[NB][Cfg<D>::BN / 32]) {
-  qk_tile<D, NB>(Kc, qf, sacc, [](int) {});
 }
 
 // Tile geometry of flattened tile index t over the (up to two) key segments.
@@ -436,25 +429,24 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 
     // prefetch: K of tile it+2 into the LDS buffer of K of tile it (read in the
     // previous iteration) and V of tile it+1 into that of V of tile it-1. The
-    // copies are spread over the k-steps of the next tile's QK^T rather than
-    // issued together: eight waves issuing them at once queue on the CU's load
-    // path (about 62 bytes per clock) with nothing else to run.
+    // copies are spread over the MFMAs of the next tile's QK^T (copy_after(i)
+    // follows product i) rather than issued together: eight waves issuing them
+    // at once queue on the CU's load path (about 62 bytes per clock) with
+    // nothing else to run.
     constexpr int KN = StageMap<D>::KN;
     const u32x4_t rk = uniform_words(kd), rv = uniform_words(vd);
-    auto copy_after = [&](int ks) {
+    auto copy_after = [&](int i) {
 #pragma unroll
       for (int j = 0; j < 2 * KN; ++j)
-        if (j * KS / (2 * KN) == ks) {
+        if (j * KS * MB / (2 * KN) == i) {
           if (j < KN) dma_1k(smap.k[j], rk, Ks[cur] + (wave * KN + j) * 512);
           else dma_1k(smap.v[j - KN], rv, Vt[cur ^ 1] + (wave * KN + j - KN) * 512);
         }
     };
 
-    f32x16_t sacc[NB][MB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sacc[nb][mb] = snext[nb][mb];
+    // this tile's scores are used in place: a block's next-tile QK^T starts
+    // only after the block's exponentials have read it
+    f32x16_t (&sacc)[NB][MB] = snext;
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -502,13 +494,15 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     for (int nb = 0; nb < NB; ++nb) mref[nb] = (m_ref[nb] == kNegInf) ? 0.f : m_ref[nb] * sl2;
 
     // ---- one scheduling region: QK^T of the next tile (matrix cores) with this
-    // tile's exponentials (vector ALUs), then this tile's PV product
-    qk_tile<D, NB>(Ks[cur ^ 1], qf, snext, copy_after);
+    // tile's exponentials (vector ALUs), then this tile's PV product. The
+    // scores stay in the registers the next QK^T writes, so each 32-key block
+    // is exponentiated before its next-tile product starts (no copy of the
+    // scores, which would sit in the phase where both waves of a SIMD run
+    // vector work only)
     uint32_t pk[NB][MB][8];
+    auto exps_block = [&](int mb) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = exp2_fast(fmaf(sacc[nb][mb][r], sl2, -mref[nb]));
@@ -518,6 +512,26 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
           l_run[nb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[nb][mb][r >> 1]), ones,
                                                       l_run[nb], false);
         }
+    };
+    // exponentials of block 0; then, per 32-key block, the next tile's QK^T
+    // (matrix cores) beside the exponentials of the following block
+    const __bf16 *Kn = Ks[cur ^ 1];
+    exps_block(0);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int key = mb * 32 + qi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = ks * 2 + hf;
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kn[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          snext[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], ks == 0 ? f32x16_t{} : snext[nb][mb],
+                                                                 0, 0, 0);
+        copy_after(mb * KS + ks);
+      }
+      if (mb + 1 < MB) exps_block(mb + 1);
+    }
     const __bf16 *Vc = Vt[cur];
 #pragma unroll
     for (int ks = 0; ks < PKS; ++ks) {
