@@ -1026,6 +1026,8 @@ bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || 
 int rows_per_unit(int dtype, int d, int rep) {
   if (!use_mfma(dtype, d)) return 1;
   if (d == 512) return 32 * (Cfg<512>::NW / Cfg<512>::NS) / pick_hg_d(512, rep);
+  // the kernel's query rows per workgroup, BM = 32 NB NW / HG, for its own head_dim
+  if (d == 64) return 32 * Cfg<64>::NB * Cfg<64>::NW / pick_hg(rep);
   return 32 * Cfg<128>::NB * Cfg<128>::NW / pick_hg(rep);
 }
 
