@@ -102,6 +102,12 @@ struct Cfg<512> {
 };
 template <int D>
 constexpr int kThreadsOf = 64 * Cfg<D>::NW;
+// Query rows of one workgroup: the kernels use these, and the host tiles every
+// chunk by the same numbers.
+template <int D, int HG>
+constexpr int kRowsMfma = 32 * Cfg<D>::NB * Cfg<D>::NW / HG;
+template <int HG>
+constexpr int kRowsWide = 32 * (Cfg<512>::NW / Cfg<512>::NS) / HG;
 
 // Per-thread byte offsets (relative to the first key row of a tile) of the
 // buffer-to-LDS copies of a K and a V tile. Lane L of a wave writes bytes
@@ -292,7 +298,7 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
   constexpr int NB = Cfg<D>::NB;                // 32-row blocks per wave
   constexpr int MB = BN / 32;                   // 32-key blocks per tile
   constexpr int PKS = BN / 16;                  // 16-key MFMA k-steps of the PV product
-  constexpr int BM = 32 * NB * NW / HG;         // query rows per workgroup
+  constexpr int BM = kRowsMfma<D, HG>;          // query rows per workgroup
   constexpr int KS = D / 16;                    // MFMA k-steps for QK^T
   constexpr int DB = D / 32;                    // 32-wide d blocks of the output
   constexpr int KSZ = BN * D;                   // K tile (bf16 elements)
@@ -617,8 +623,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   constexpr int D = 512;
   constexpr int BN = Cfg<D>::BN;                // 32 keys per tile
   constexpr int NS = Cfg<D>::NS;                // waves per row block
-  constexpr int NG = Cfg<D>::NW / NS;           // row blocks (groups) per workgroup
-  constexpr int BM = 32 * NG / HG;              // query rows per workgroup
+  constexpr int BM = kRowsWide<HG>;             // query rows per workgroup
   constexpr int DW = D / NS;                    // columns of d per wave
   constexpr int KSH = DW / 16;                  // QK^T k-steps over a wave's columns
   constexpr int DBH = DW / 32;                  // output d blocks of a wave
@@ -1023,12 +1028,18 @@ hipError_t launch_generic(const SeqTable &t, const StepArgs &a, int units, hipSt
 // The MFMA kernel covers bf16 (head_dim 64, 128, 512); fp32 runs the generic kernel.
 bool use_mfma(int dtype, int d) { return dtype == CPATTN_DT_BF16 && (d == 64 || d == 128 || d == 512); }
 
+template <int D>
+int rows_mfma(int hg) {
+  return hg == 4 ? kRowsMfma<D, 4> : hg == 2 ? kRowsMfma<D, 2> : kRowsMfma<D, 1>;
+}
+
+// rows per work unit of the kernel that launch() runs for (dtype, d, rep), with
+// the head grouping launch_mfma_d picks
 int rows_per_unit(int dtype, int d, int rep) {
   if (!use_mfma(dtype, d)) return 1;
-  if (d == 512) return 32 * (Cfg<512>::NW / Cfg<512>::NS) / pick_hg_d(512, rep);
-  // the kernel's query rows per workgroup, BM = 32 NB NW / HG, for its own head_dim
-  if (d == 64) return 32 * Cfg<64>::NB * Cfg<64>::NW / pick_hg(rep);
-  return 32 * Cfg<128>::NB * Cfg<128>::NW / pick_hg(rep);
+  if (d == 512) return pick_hg_d(512, rep) == 2 ? kRowsWide<2> : kRowsWide<1>;
+  const int hg = pick_hg(rep);
+  return d == 64 ? rows_mfma<64>(hg) : rows_mfma<128>(hg);
 }
 
 hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
