@@ -62,8 +62,8 @@ def _decode_cases(n, seed=2025):
     return out
 
 
-PREFILL = _prefill_cases(24)
-DECODE = _decode_cases(16)
+PREFILL = _prefill_cases(48)
+DECODE = _decode_cases(32)
 
 
 def _padded_locals(ca, cu, cp, tensors):
