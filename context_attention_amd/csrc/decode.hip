@@ -918,8 +918,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void decode_reduce(ReduceArgs a) {
 }
 
 // Split geometry: about `target` workgroups over the `groups` (shard, batch
-// entry, head block) triples, at least 4 rounds of `step` keys per split, and
-// split lengths that are whole rounds.
+// entry, head block) triples, split lengths that are whole rounds of `step`
+// keys, and no more splits than a quarter of the shard's rounds (so a shard
+// that is split at all gets at least 3 rounds per split).
 void plan_splits(int64_t shard_len, int64_t step, int64_t groups, int64_t target, int32_t &nsplit,
                  int64_t &split_len) {
   int64_t want = (target + groups - 1) / groups;
