@@ -980,7 +980,9 @@ DecodePlan plan_decode(const cpattn_decode_desc &d) {
   } else {
     const int64_t step = (int64_t)(64 / (d.head_dim / 8)) * kDecWaves * kUnroll;
     const int64_t groups = (int64_t)d.cp * d.batch * (d.n_hq / p.gv);
-    plan_splits(shard_len, step, groups, 4096, p.nsplit, p.split_len);
+    // about 8192 workgroups for the vector kernel (measured on MI355X: +2% on
+    // GQA 32/8 d128 over 4096, level at batch 2, slower at 16384 and beyond)
+    plan_splits(shard_len, step, groups, 8192, p.nsplit, p.split_len);
   }
   return p;
 }

@@ -59,7 +59,7 @@ int main() {
               } else {
                 step = (int64_t)(64 / (D / 8)) * kDecWaves * kUnroll;
                 groups = (int64_t)cp * b * (d.n_hq / p.gv);
-                target = 4096;
+                target = 8192;
               }
               CHECK(p.nsplit >= 1, "D%d cp%d b%d len%lld %d/%d: nsplit %d\n", D, cp, b, (long long)per_shard, hl[0],
                     hl[1], p.nsplit);
