@@ -255,12 +255,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial(DecodeArgs a) {
 // O^T = V^T P^T (v_mfma_f32_32x32x16_bf16); each lane owns one head, so the
 // softmax needs one cross-lane exchange per 32-key tile. Heads past the group
 // are zero columns that are not stored.
-//   head_dim 64 / 128: KG = 4 / 2 waves; wave w streams the split's 32-key tiles
-//     w, w + KG, ... through its own ring of NST = 4 LDS buffers (buffer-to-LDS
-//     copies of whole rows, three tiles in flight while one computes: the HBM
-//     latency is covered by bytes in flight, which the LDS bounds), so the key
-//     loop has no barrier; the KG partial triples are merged through LDS at the
-//     end.
+//   head_dim 64 / 128: KG = 8 / 4 waves; wave w streams the split's 32-key tiles
+//     w, w + KG, ... through its own ring of NST = 2 LDS buffers (buffer-to-LDS
+//     copies of whole rows, one tile in flight while one computes: the HBM
+//     latency is covered by bytes in flight, which the LDS bounds, and the KG
+//     waves share them out), so the key loop has no barrier; the KG partial
+//     triples are merged through LDS at the end.
 //   head_dim 512: a quad of waves, each owning a quarter of d and copying only
 //     that quarter of every tile (32 + 64 registers of Q and accumulator); the
 //     four partial score tiles are exchanged through LDS and summed in one fixed
@@ -271,11 +271,11 @@ template <int D>
 struct DecCfg;
 template <>
 struct DecCfg<64> {
-  static constexpr int DS = 1, KG = 4, NST = 4;
+  static constexpr int DS = 1, KG = 8, NST = 2;
 };
 template <>
 struct DecCfg<128> {
-  static constexpr int DS = 1, KG = 2, NST = 4;
+  static constexpr int DS = 1, KG = 4, NST = 2;
 };
 template <>
 struct DecCfg<512> {
