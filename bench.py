@@ -91,46 +91,43 @@ def measured_traffic(kernel):
     return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
 
 
-def overlap_report(ca, synth, torch, pdesc, q0, blocks):
-    """Pass-KV ring with its block transfers on a DMA copy engine beside the
-    ring steps (cpattn_ring_prefill_overlapped, three receive buffers), after
-    the timed steps: the headline rank-0 share (the spec's large-S/cp
-    metamorphic check, < 10% from pure compute) and a middle-band ring (MHA,
-    64 heads, S=16384, cp=8, rank 3; transfer/compute ratio in [0.5, 2]). Both
-    run on the dedicated stream pair that a probe of the middle-band ring finds
-    fastest (overlap.stream_pair); the probe's spread is reported."""
+def overlap_report(ca, synth, torch):
+    """The pass-KV ring of the whole CP group with its block transfers beside
+    the ring steps (cpattn_ring_prefill_overlapped, three receive buffers per
+    rank), after the timed steps. The link is the copy kernel on a few compute
+    units set apart by CU masks (overlap.link_streams), about one xGMI link's
+    rate. Reported: the spec's middle-band check on the GQA prefill workload
+    (S=32768, cp=8; transfer/compute ratio in [0.5, 2]) and its large-S/cp
+    metamorphic check on S=262144, cp=8 with the same heads (< 10% from pure
+    compute)."""
     ov = ca.overlap
-    w = synth.PrefillWorkload(name="mha 16384", seqlens=[16384], cp=8, n_hq=64, n_kv=64, head_dim=128,
-                              dtype="bf16", scale_in=0.5, seed=1)
-    S = w.total_tokens
-    full = [synth.tensor_torch(w.seed, t, (S, w.n_hq, w.head_dim), w.scale_in, w.dtype, "cuda")
-            for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V)]
-    kb, vb, q3 = [], [], None
-    for j in range(w.cp):
-        idx = torch.from_numpy(ca.balanced_split(w.cu_seqlens, w.cp, j)[0]).to("cuda")
-        kb.append(full[1].index_select(0, idx).contiguous())
-        vb.append(full[2].index_select(0, idx).contiguous())
-        if j == 3:
-            q3 = full[0].index_select(0, idx).contiguous()
-    del full
-    desc = ca.PrefillDesc(cp=w.cp, cu_seqlens=w.cu_seqlens, n_hq=w.n_hq, n_kv=w.n_kv, head_dim=w.head_dim,
-                          dtype=w.dtype, scale=w.softmax_scale)
-    xb = ov.make_inputs(desc, 3, q3, kb, vb, n_recv=3)
-    log("bench: overlap, choosing the stream pair")
-    comp, xfer, probes = ov.stream_pair(xb, 0)
-    log("bench: overlap, headline share")
-    x = ov.make_inputs(pdesc, 0, q0, [k for k, _ in blocks], [v for _, v in blocks], n_recv=3)
-    meta = ov.overlap_metamorphic(x, 0, comp, xfer, reps=1)
-    del x
-    log("bench: overlap, middle band")
-    band = ov.overlap_effective(xb, 0, comp, xfer, reps=5)
-    rnd = lambda d: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items() if k != "workgroups"}
-    pt = sorted(probes.values())
-    return {"transfer": "DMA copy engine", "receive_buffers": 3,
-            "stream_pair_probe_ms": {"best": round(pt[0], 4), "median": round(pt[len(pt) // 2], 4),
-                                     "worst": round(pt[-1], 4), "pairs": len(pt)},
-            "headline_share": rnd(meta),
-            "middle_band": dict(workload="MHA 64 heads, d128, S=16384, cp=8, rank 3", **rnd(band))}
+    comp, xfer = ov.link_streams(ov.LINK_CUS)
+    rnd = lambda d: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+    res = {"transfer": f"copy kernel, {ov.LINK_WORKGROUPS} workgroups on {ov.LINK_CUS} CUs set apart by CU masks",
+           "receive_buffers": 3}
+    for key, w, fn in (("middle_band", synth.WORKLOADS["gqa"], ov.overlap_effective),
+                       ("large_block", synth.PrefillWorkload(name="gqa 256k", seqlens=[262144], cp=8, n_hq=32,
+                                                             n_kv=8, head_dim=128, dtype="bf16", scale_in=0.5,
+                                                             seed=1), ov.overlap_metamorphic)):
+        log(f"bench: overlap, {key}")
+        S = w.total_tokens
+        full = [synth.tensor_torch(w.seed, t, (S, h, w.head_dim), w.scale_in, w.dtype, "cuda")
+                for t, h in ((synth.TENSOR_Q, w.n_hq), (synth.TENSOR_K, w.n_kv), (synth.TENSOR_V, w.n_kv))]
+        qs, ks, vs = [], [], []
+        for j in range(w.cp):
+            idx = torch.from_numpy(ca.balanced_split(w.cu_seqlens, w.cp, j)[0]).to("cuda")
+            for lst, t in zip((qs, ks, vs), full):
+                lst.append(t.index_select(0, idx).contiguous())
+        del full
+        desc = ca.PrefillDesc(cp=w.cp, cu_seqlens=w.cu_seqlens, n_hq=w.n_hq, n_kv=w.n_kv, head_dim=w.head_dim,
+                              dtype=w.dtype, scale=w.softmax_scale)
+        x = ov.make_inputs(desc, qs, ks, vs, n_recv=3)
+        r = fn(x, ov.LINK_WORKGROUPS, comp, xfer, reps=5 if key == "middle_band" else 2)
+        r.pop("workgroups")
+        res[key] = dict(workload=f"S={S}, cp={w.cp}, {w.n_hq}q/{w.n_kv}kv, d{w.head_dim}, all ranks", **rnd(r))
+        del x, qs, ks, vs
+        torch.cuda.empty_cache()
+    return res
 
 
 def _full_ring_tflops(ca, synth, torch, w, reps=3):
@@ -398,7 +395,7 @@ def main():
     }
     del kshards, vshards
     if not args.no_overlap:
-        res["overlap"] = overlap_report(ca, synth, torch, pdesc, q0, blocks)
+        res["overlap"] = overlap_report(ca, synth, torch)
     del blocks
     torch.cuda.empty_cache()
     if not args.no_configs:

@@ -6,8 +6,8 @@ streams. The binding fails loudly when the library has not been built; there
 is no fallback path.
 
 Entry points mirror the C names of include/cpattn.h:
-    balanced_split, balanced_split_padded, ring_step_partial, ring_pass, ring_prefill_overlapped,
-    merge, tree_reduce, passq_decode, account
+    balanced_split, balanced_split_padded, local_rows, ring_step_partial, ring_pass,
+    ring_prefill_overlapped, merge, tree_reduce, passq_decode, account
 """
 from __future__ import annotations
 
@@ -20,9 +20,9 @@ import numpy as np
 
 __all__ = [
     "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
-    "balanced_split", "balanced_split_padded", "padded_rows", "ring_step_partial", "ring_pass",
+    "balanced_split", "balanced_split_padded", "local_rows", "padded_rows", "ring_step_partial", "ring_pass",
     "ring_prefill_overlapped", "merge", "tree_reduce", "passq_decode", "passq_workspace_bytes",
-    "account", "new_partial",
+    "account", "new_partial", "RingEvents",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,8 @@ _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPP
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
 
-EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_ring_step_partial", "cpattn_ring_pass",
+EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_local_rows", "cpattn_ring_step_partial",
+           "cpattn_ring_pass",
            "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_tree_reduce", "cpattn_passq_decode",
            "cpattn_account", "cpattn_version"]
 
@@ -98,12 +99,14 @@ def load():
     lib.cpattn_balanced_split.argtypes = [ctypes.POINTER(ctypes.c_int64), i32, i32, i32,
                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.cpattn_balanced_split_padded.argtypes = lib.cpattn_balanced_split.argtypes
+    lib.cpattn_local_rows.argtypes = [ctypes.POINTER(ctypes.c_int64), i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.cpattn_ring_step_partial.argtypes = [ctypes.POINTER(_PrefillDesc), i32, i32, vp, vp, vp,
                                              ctypes.POINTER(_Partial), i32, vp]
     lib.cpattn_ring_pass.argtypes = [vp, vp, i64, i32, vp]
-    lib.cpattn_ring_prefill_overlapped.argtypes = [ctypes.POINTER(_PrefillDesc), i32, vp, ctypes.POINTER(vp),
-                                                   ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), i32,
-                                                   ctypes.POINTER(_Partial), i32, vp, vp]
+    lib.cpattn_ring_prefill_overlapped.argtypes = [ctypes.POINTER(_PrefillDesc), ctypes.POINTER(vp),
+                                                   ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                                   ctypes.POINTER(vp), i32, ctypes.POINTER(_Partial), i32, vp, vp,
+                                                   ctypes.POINTER(vp), i32]
     lib.cpattn_merge.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, ctypes.POINTER(_Partial),
                                  vp, vp, vp]
     lib.cpattn_tree_reduce.argtypes = [i64, i32, i32, ctypes.POINTER(_Partial), i32, vp, vp, vp]
@@ -160,10 +163,20 @@ def balanced_split_padded(cu_seqlens, cp: int, rank: int):
     return pos[:rows], cul
 
 
+def local_rows(cu_seqlens, cp: int, padded: bool = False) -> int:
+    """cpattn_local_rows: rows of one rank's local buffers (pad rows included
+    when `padded`)."""
+    lib = load()
+    cu = _i64_array(cu_seqlens)
+    out = ctypes.c_int64(0)
+    _check(lib.cpattn_local_rows(_i64_ptr(cu), cu.size - 1, cp, int(bool(padded)), ctypes.byref(out)),
+           "cpattn_local_rows")
+    return int(out.value)
+
+
 def padded_rows(cu_seqlens, cp: int) -> int:
     """Local rows of one rank when every sequence is padded to a multiple of 2*cp."""
-    L = np.diff(_i64_array(cu_seqlens))
-    return int(np.sum(2 * ((L + 2 * cp - 1) // (2 * cp))))
+    return local_rows(cu_seqlens, cp, padded=True)
 
 
 def account(*, cp: int, n_hq: int, n_kv: int, head_dim: int, dtype_bytes: int, cu_seqlens=None,
@@ -218,9 +231,7 @@ class PrefillDesc:
     @property
     def rows(self) -> int:
         """Rows of one rank's local buffers (pad rows included)."""
-        if self.padded:
-            return padded_rows(self.cu_seqlens, self.cp)
-        return int(np.asarray(self.cu_seqlens)[-1]) // self.cp
+        return local_rows(self.cu_seqlens, self.cp, self.padded)
 
     def _c(self):
         cu = _i64_array(self.cu_seqlens)
@@ -275,18 +286,25 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _check_partial(p: Partial, rows: int, n_hq: int, head_dim: int, what: str) -> None:
+    """Shapes of a triple for rows x n_hq (row, head) pairs."""
+    if tuple(p.m.shape) != (rows, n_hq) or tuple(p.den.shape) != (rows, n_hq) \
+            or tuple(p.num.shape) != (rows, n_hq, head_dim):
+        raise ValueError(f"{what} shape mismatch: m {tuple(p.m.shape)}, den {tuple(p.den.shape)}, "
+                         f"num {tuple(p.num.shape)}; expected ({rows}, {n_hq}) and ({rows}, {n_hq}, {head_dim})")
+
+
 def ring_step_partial(desc: PrefillDesc, rank: int, step: int, q_local, k_blk, v_blk, dst: Partial,
                       accumulate: bool = False, stream=None) -> None:
     """cpattn_ring_step_partial (see include/cpattn.h)."""
     lib = load()
     rows = desc.rows
     for t, h in ((q_local, desc.n_hq), (k_blk, desc.n_kv), (v_blk, desc.n_kv)):
-        _dev_check(t, desc.dtype)
         if tuple(t.shape) != (rows, h, desc.head_dim):
             raise ValueError(f"shape {tuple(t.shape)} != {(rows, h, desc.head_dim)}")
-    if tuple(dst.num.shape) != (rows, desc.n_hq, desc.head_dim) or tuple(dst.m.shape) != (rows, desc.n_hq) \
-            or tuple(dst.den.shape) != (rows, desc.n_hq):
-        raise ValueError("dst shape mismatch")
+    _check_partial(dst, rows, desc.n_hq, desc.head_dim, "dst")
+    for t in (q_local, k_blk, v_blk):
+        _dev_check(t, desc.dtype)
     d, keep = desc._c()
     p = dst._c()
     _check(lib.cpattn_ring_step_partial(ctypes.byref(d), rank, step, q_local.data_ptr(), k_blk.data_ptr(),
@@ -308,51 +326,87 @@ def ring_pass(src, dst, workgroups: int, stream=None) -> None:
            "cpattn_ring_pass")
 
 
-def ring_prefill_overlapped(desc: PrefillDesc, rank: int, q_local, k_blocks: Sequence, v_blocks: Sequence,
-                            k_recv: Sequence, v_recv: Sequence, acc: Partial, link_workgroups: int,
-                            compute_stream=None, transfer_stream=None) -> None:
-    """cpattn_ring_prefill_overlapped (see include/cpattn.h): the cp ring steps of
-    `rank` on compute_stream, the block transfers into the receive buffers
-    k_recv / v_recv (two or more each) on transfer_stream."""
+class RingEvents:
+    """HIP events owned by the caller of cpattn_ring_prefill_overlapped (2*cp of
+    them, created with hipEventDisableTiming on the current device, destroyed
+    with this object)."""
+
+    def __init__(self, count: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._vp = ctypes.c_void_p      # kept for __del__, which can run at interpreter exit
+        self.handles = (ctypes.c_void_p * count)()
+        self.count = 0
+        for i in range(count):
+            rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.handles, i * ctypes.sizeof(ctypes.c_void_p)),
+                                                   ctypes.c_uint(2))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed with HIP error {rc}")
+            self.count += 1
+
+    def __del__(self):
+        hip, vp = getattr(self, "_hip", None), getattr(self, "_vp", None)
+        if hip is None or vp is None:
+            return
+        for i in range(getattr(self, "count", 0)):
+            hip.hipEventDestroy(vp(self.handles[i]))
+
+
+def ring_prefill_overlapped(desc: PrefillDesc, q_local: Sequence, k_blocks: Sequence, v_blocks: Sequence,
+                            k_recv: Sequence, v_recv: Sequence, acc: Sequence[Partial], link_workgroups: int,
+                            compute_stream=None, transfer_stream=None, events: Optional[RingEvents] = None) -> None:
+    """cpattn_ring_prefill_overlapped (see include/cpattn.h): the whole ring of the
+    CP group, rank r's steps on compute_stream on the block in hand, every block
+    forwarded to the next rank's receive buffers on transfer_stream. q_local,
+    k_blocks, v_blocks and acc hold one entry per rank; k_recv and v_recv hold
+    cp * n_recv buffers, rank-major. `events` (2*cp of them) are created for
+    the call when not given."""
     lib = load()
+    cp = desc.cp
     rows = desc.rows
-    if len(k_blocks) != desc.cp or len(v_blocks) != desc.cp:
-        raise ValueError("need cp K and V blocks")
-    if len(k_recv) != len(v_recv) or len(k_recv) < 2:
-        raise ValueError("need as many K as V receive buffers, at least two")
-    _dev_check(q_local, desc.dtype)
-    if tuple(q_local.shape) != (rows, desc.n_hq, desc.head_dim):
-        raise ValueError("q_local shape mismatch")
+    if len(q_local) != cp or len(k_blocks) != cp or len(v_blocks) != cp or len(acc) != cp:
+        raise ValueError("need cp queries, K and V blocks and accumulators")
+    if len(k_recv) != len(v_recv) or len(k_recv) % cp or (cp > 1 and len(k_recv) // cp < 2):
+        raise ValueError("need cp * n_recv K and V receive buffers, n_recv >= 2")
+    n_recv = len(k_recv) // cp
+    for t in q_local:
+        if tuple(t.shape) != (rows, desc.n_hq, desc.head_dim):
+            raise ValueError(f"q_local shape {tuple(t.shape)} != {(rows, desc.n_hq, desc.head_dim)}")
     for t in list(k_blocks) + list(v_blocks) + list(k_recv) + list(v_recv):
-        _dev_check(t, desc.dtype)
         if tuple(t.shape) != (rows, desc.n_kv, desc.head_dim):
             raise ValueError(f"block shape {tuple(t.shape)} != {(rows, desc.n_kv, desc.head_dim)}")
-    if tuple(acc.num.shape) != (rows, desc.n_hq, desc.head_dim):
-        raise ValueError("acc shape mismatch")
+    for p in acc:
+        _check_partial(p, rows, desc.n_hq, desc.head_dim, "acc")
+    for t in list(q_local) + list(k_blocks) + list(v_blocks) + list(k_recv) + list(v_recv):
+        _dev_check(t, desc.dtype)
+    if events is None:
+        events = RingEvents(2 * cp)
+    if events.count < 2 * cp:
+        raise ValueError(f"need {2 * cp} events")
     d, keep = desc._c()
-    p = acc._c()
-    arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
-    _check(lib.cpattn_ring_prefill_overlapped(ctypes.byref(d), rank, q_local.data_ptr(), arr(k_blocks),
-                                              arr(v_blocks), arr(k_recv), arr(v_recv), len(k_recv), ctypes.byref(p),
-                                              link_workgroups, _stream(compute_stream),
-                                              _stream(transfer_stream)), "cpattn_ring_prefill_overlapped")
+    parts = (_Partial * cp)(*[p._c() for p in acc])
+    arr = lambda ts: (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+    _check(lib.cpattn_ring_prefill_overlapped(ctypes.byref(d), arr(q_local), arr(k_blocks), arr(v_blocks),
+                                              arr(k_recv), arr(v_recv), n_recv, parts, link_workgroups,
+                                              _stream(compute_stream), _stream(transfer_stream), events.handles,
+                                              events.count), "cpattn_ring_prefill_overlapped")
 
 
 def merge(acc: Partial, parts: Sequence[Partial] = (), out=None, lse=None, stream=None) -> None:
     """cpattn_merge: acc = merge(acc, *parts); optionally out = num/den, lse = m + ln den."""
     lib = load()
+    if acc.num.dim() != 3:
+        raise ValueError("acc.num must be [rows, n_hq, head_dim]")
     rows, n_hq, hd = acc.num.shape
+    _check_partial(acc, rows, n_hq, hd, "acc")
     for p in parts:
-        if p.num.shape != acc.num.shape or p.m.shape != acc.m.shape:
-            raise ValueError("part shape mismatch")
-    if out is not None:
-        _dev_check(out, "f32")
-        if tuple(out.shape) != (rows, n_hq, hd):
-            raise ValueError("out shape mismatch")
-    if lse is not None:
-        _dev_check(lse, "f32")
-        if tuple(lse.shape) != (rows, n_hq):
-            raise ValueError("lse shape mismatch")
+        _check_partial(p, rows, n_hq, hd, "part")
+    if out is not None and tuple(out.shape) != (rows, n_hq, hd):
+        raise ValueError("out shape mismatch")
+    if lse is not None and tuple(lse.shape) != (rows, n_hq):
+        raise ValueError("lse shape mismatch")
+    for t in (out, lse):
+        if t is not None:
+            _dev_check(t, "f32")
     arr = (_Partial * max(len(parts), 1))(*[p._c() for p in parts])
     a = acc._c()
     _check(lib.cpattn_merge(rows, n_hq, hd, arr if parts else None, len(parts), ctypes.byref(a),
@@ -367,18 +421,18 @@ def tree_reduce(parts: Sequence[Partial], out=None, lse=None, stream=None) -> No
     lib = load()
     if not parts:
         raise ValueError("at least one part")
+    if parts[0].num.dim() != 3:
+        raise ValueError("num must be [rows, n_hq, head_dim]")
     rows, n_hq, hd = parts[0].num.shape
     for p in parts:
-        if p.num.shape != parts[0].num.shape or p.m.shape != parts[0].m.shape:
-            raise ValueError("part shape mismatch")
-    if out is not None:
-        _dev_check(out, "f32")
-        if tuple(out.shape) != (rows, n_hq, hd):
-            raise ValueError("out shape mismatch")
-    if lse is not None:
-        _dev_check(lse, "f32")
-        if tuple(lse.shape) != (rows, n_hq):
-            raise ValueError("lse shape mismatch")
+        _check_partial(p, rows, n_hq, hd, "part")
+    if out is not None and tuple(out.shape) != (rows, n_hq, hd):
+        raise ValueError("out shape mismatch")
+    if lse is not None and tuple(lse.shape) != (rows, n_hq):
+        raise ValueError("lse shape mismatch")
+    for t in (out, lse):
+        if t is not None:
+            _dev_check(t, "f32")
     arr = (_Partial * len(parts))(*[p._c() for p in parts])
     _check(lib.cpattn_tree_reduce(rows, n_hq, hd, arr, len(parts),
                                   out.data_ptr() if out is not None else None,
@@ -402,18 +456,22 @@ def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, sh
     import torch
     lib = load()
     b, hq, hd = desc.batch, desc.n_hq, desc.head_dim
-    _dev_check(q, desc.dtype)
     if tuple(q.shape) != (b, hq, hd):
         raise ValueError("q shape mismatch")
     if len(k_shards) != desc.cp or len(v_shards) != desc.cp:
         raise ValueError("need cp K and V shards")
     shard_len = desc.kv_len // desc.cp
     for t in list(k_shards) + list(v_shards):
-        _dev_check(t, desc.dtype)
         if tuple(t.shape) != (b, shard_len, desc.n_kv, hd):
             raise ValueError(f"shard shape {tuple(t.shape)} != {(b, shard_len, desc.n_kv, hd)}")
-    if tuple(shard_partials.num.shape) != (desc.cp * b, hq, hd):
-        raise ValueError("shard_partials shape mismatch")
+    _check_partial(shard_partials, desc.cp * b, hq, hd, "shard_partials")
+    if tuple(out.shape) != (b, hq, hd):
+        raise ValueError(f"out shape {tuple(out.shape)} != {(b, hq, hd)}")
+    if tuple(lse.shape) != (b, hq):
+        raise ValueError(f"lse shape {tuple(lse.shape)} != {(b, hq)}")
+    _dev_check(q, desc.dtype)
+    for t in list(k_shards) + list(v_shards):
+        _dev_check(t, desc.dtype)
     _dev_check(out, "f32")
     _dev_check(lse, "f32")
     need = passq_workspace_bytes(desc)

@@ -87,6 +87,20 @@ extern "C" int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t n
   return CPATTN_OK;
 }
 
+extern "C" int cpattn_local_rows(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t padded,
+                                 int64_t *rows) {
+  // rows of one rank's local buffers: sum over sequences of 2 c_i, with
+  // c_i = L_i / (2 cp), or ceil(L_i / (2 cp)) in the padded layout
+  if (cp < 1 || rows == nullptr || (padded != 0 && padded != 1)) return CPATTN_E_ARG;
+  const int64_t two_cp = 2 * (int64_t)cp;
+  const int rc = check_seqlens(cu_seqlens, num_seqs, padded ? 1 : two_cp);
+  if (rc != CPATTN_OK) return rc;
+  int64_t r = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) r += 2 * ((cu_seqlens[i + 1] - cu_seqlens[i] + two_cp - 1) / two_cp);
+  *rows = r;
+  return CPATTN_OK;
+}
+
 extern "C" int cpattn_account(const cpattn_account_in *in, cpattn_account_out *out) {
   if (in == nullptr || out == nullptr) return CPATTN_E_ARG;
   const int64_t cp = in->cp;

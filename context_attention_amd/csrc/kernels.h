@@ -81,6 +81,10 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float &m, floa
 // entry points (CPATTN_OK or the error code; no device call).
 __attribute__((visibility("hidden"))) int check_prefill(const cpattn_prefill_desc *desc, int32_t rank,
                                                           int32_t step);
+// CPATTN_OK when every sequence of a description check_prefill accepted fits
+// the ring-step launches (the error cpattn_ring_step_partial would return
+// otherwise, before launching anything).
+__attribute__((visibility("hidden"))) int check_launches(const cpattn_prefill_desc *desc);
 // Rows of one rank's local buffers (sum over sequences of 2 c_i, pad rows
 // included) for a description check_prefill accepted.
 __attribute__((visibility("hidden"))) int64_t local_rows(const cpattn_prefill_desc *desc);

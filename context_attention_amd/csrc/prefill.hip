@@ -1053,8 +1053,55 @@ hipError_t launch(int dtype, int d, const SeqTable &t, const StepArgs &a, int un
   return launch_generic<float, 512>(t, a, units, s);
 }
 
+// Sequences go into launches of at most kMaxSeq sequences and 2^31 - 1
+// workgroups. With a == nullptr the partition is only checked:
+// hipErrorInvalidValue when a single sequence needs more workgroups than one
+// launch holds. cpattn_ring_step_partial checks before it launches, so that an
+// error leaves no work enqueued.
+hipError_t run_launches(const cpattn_prefill_desc *desc, const StepArgs *a, hipStream_t stream) {
+  const int cp = desc->cp;
+  const int d = desc->head_dim;
+  const int64_t *cu = desc->cu_seqlens;
+  const int rep = desc->n_hq / desc->n_kv;
+  const int rpu = rows_per_unit(desc->dtype, d, rep);
+  const bool mfma = use_mfma(desc->dtype, d);
+  const int64_t groups = mfma ? desc->n_hq / pick_hg_d(d, rep) : 1;
+  int i = 0;
+  int64_t row_off = 0;
+  while (i < desc->num_seqs) {
+    SeqTable t;
+    t.n = 0;
+    t.start[0] = 0;
+    int64_t units = 0;
+    while (i < desc->num_seqs && t.n < kMaxSeq) {
+      const int64_t L = cu[i + 1] - cu[i];
+      const int64_t c = (L + 2 * cp - 1) / (2 * cp);   // = L / (2 cp) unless padded
+      const int64_t u = mfma ? 2 * ((c + rpu - 1) / rpu) : 2 * c;
+      const int64_t blocks_after = (units + u) * groups;
+      if (t.n > 0 && blocks_after > 0x7FFFFFFFLL) break;
+      if (blocks_after > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+      t.c[t.n] = (int32_t)c;
+      t.len[t.n] = (int32_t)L;
+      t.row_off[t.n] = row_off;
+      units += u;
+      t.start[t.n + 1] = (int32_t)units;
+      row_off += 2 * c;
+      ++t.n;
+      ++i;
+    }
+    if (a == nullptr || units == 0) continue;
+    const hipError_t e = launch(desc->dtype, d, t, *a, (int)units, stream);
+    if (e != hipSuccess) return e == hipErrorInvalidValue ? hipErrorLaunchFailure : e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 }  // namespace cpattn
+
+int cpattn::check_launches(const cpattn_prefill_desc *desc) {
+  return run_launches(desc, nullptr, nullptr) == hipSuccess ? CPATTN_OK : CPATTN_E_UNSUPPORTED;
+}
 
 int cpattn::check_prefill(const cpattn_prefill_desc *desc, int32_t rank, int32_t step) {
   if (desc == nullptr) return CPATTN_E_ARG;
@@ -1099,7 +1146,6 @@ extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t
   if (chk != CPATTN_OK) return chk;
   if (accumulate != 0 && accumulate != 1) return CPATTN_E_ARG;
   const int cp = desc->cp;
-  const int d = desc->head_dim;
   const int64_t *cu = desc->cu_seqlens;
   const int64_t total = desc->num_seqs > 0 ? cu[desc->num_seqs] : 0;
   if (total == 0) return CPATTN_OK;
@@ -1124,36 +1170,7 @@ extern "C" int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t
   a.scale = desc->scale;
   a.accumulate = accumulate;
 
-  const int rep = desc->n_hq / desc->n_kv;
-  const int rpu = rows_per_unit(desc->dtype, d, rep);
-  const bool mfma = use_mfma(desc->dtype, d);
-  // group sequences into launches of at most kMaxSeq sequences and 2^31 blocks
-  int i = 0;
-  int64_t row_off = 0;
-  while (i < desc->num_seqs) {
-    SeqTable t;
-    t.n = 0;
-    t.start[0] = 0;
-    int64_t units = 0;
-    while (i < desc->num_seqs && t.n < kMaxSeq) {
-      const int64_t L = cu[i + 1] - cu[i];
-      const int64_t c = (L + 2 * cp - 1) / (2 * cp);   // = L / (2 cp) unless padded
-      const int64_t u = mfma ? 2 * ((c + rpu - 1) / rpu) : 2 * c;
-      const int64_t blocks_after = (units + u) * (mfma ? desc->n_hq / pick_hg_d(d, rep) : 1);
-      if (t.n > 0 && blocks_after > 0x7FFFFFFFLL) break;
-      if (blocks_after > 0x7FFFFFFFLL) return CPATTN_E_UNSUPPORTED;
-      t.c[t.n] = (int32_t)c;
-      t.len[t.n] = (int32_t)L;
-      t.row_off[t.n] = row_off;
-      units += u;
-      t.start[t.n + 1] = (int32_t)units;
-      row_off += 2 * c;
-      ++t.n;
-      ++i;
-    }
-    if (units == 0) continue;
-    const hipError_t e = launch(desc->dtype, d, t, a, (int)units, stream);
-    if (e != hipSuccess) return CPATTN_E_DEVICE;
-  }
-  return CPATTN_OK;
+  if (run_launches(desc, nullptr, nullptr) != hipSuccess) return CPATTN_E_UNSUPPORTED;
+  const hipError_t e = run_launches(desc, &a, stream);
+  return e == hipSuccess ? CPATTN_OK : CPATTN_E_DEVICE;
 }

@@ -1,4 +1,4 @@
-// Pass-KV ring of one rank on one GPU with the transfer made explicit
+// Pass-KV ring of a CP group on one GPU with the transfers made explicit
 // (G5 context-parallel modelling spec: Definitions table, "Pass-KV" and "Ring
 // step"; Rationale, the dependency contract of the ring; Acceptance,
 // "overlap effective").
@@ -11,15 +11,19 @@
 // truly runs beside a ring step: a copy kernel on another stream only gets
 // compute units once the ring step's grid has been fully dispatched.
 //
-// cpattn_ring_prefill_overlapped enqueues the whole ring of one rank on two
-// streams, with HIP events carrying exactly the edges of the contract:
-//   compute(i)  waits for transfer(i-1)   (the block it reads has arrived),
+// cpattn_ring_prefill_overlapped enqueues the whole ring of the CP group (every
+// rank emulated on the one GPU) on two streams. At step i every rank r computes
+// its partial on the block in hand and forwards that same block to rank r+1,
+// which computes on it at step i+1. HIP events carry exactly the edges of the
+// contract, step by step over the group:
+//   compute(i)  waits for transfer(i-1)   (the blocks it reads have arrived),
 //   transfer(i) follows transfer(i-1)     (it forwards what that one delivered),
 //   transfer(i) waits for compute(i+1-n)  (with n receive buffers, it
-//                                          overwrites the buffer that compute
+//                                          overwrites the buffers that compute
 //                                          read; i+1-n >= 1),
-// and no edge from compute(i) to transfer(i), so a step's transfer runs
-// concurrently with that step's compute.
+// and no edge from compute(i) to transfer(i), so a step's transfers run
+// concurrently with that step's compute. The transfers of the first step wait
+// for the work the caller enqueued on the compute stream before the call.
 #include "kernels.h"
 
 namespace cpattn {
@@ -67,21 +71,6 @@ hipError_t launch_pass(const void *src, void *dst, int64_t bytes, int32_t workgr
   return hipGetLastError();
 }
 
-struct Events {
-  hipEvent_t *e = nullptr;
-  int n = 0;
-  explicit Events(int count) : e(new hipEvent_t[count]()), n(0) {
-    for (; n < count; ++n)
-      if (hipEventCreateWithFlags(&e[n], hipEventDisableTiming) != hipSuccess) break;
-  }
-  bool ok(int count) const { return n == count; }
-  ~Events() {
-    // an event still pending on a stream is released once it completes
-    for (int i = 0; i < n; ++i) (void)hipEventDestroy(e[i]);
-    delete[] e;
-  }
-};
-
 }  // namespace
 }  // namespace cpattn
 
@@ -92,63 +81,78 @@ extern "C" int cpattn_ring_pass(const void *src, void *dst, int64_t bytes, int32
   return launch_pass(src, dst, bytes, workgroups, stream) == hipSuccess ? CPATTN_OK : CPATTN_E_DEVICE;
 }
 
-extern "C" int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, int32_t rank, const void *q_local,
+extern "C" int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, const void *const *q_local,
                                               const void *const *k_blocks, const void *const *v_blocks,
                                               void *const *k_recv, void *const *v_recv, int32_t n_recv,
                                               const cpattn_partial *acc, int32_t link_workgroups, hipStream_t compute,
-                                              hipStream_t transfer) {
+                                              hipStream_t transfer, hipEvent_t *events, int32_t n_events) {
   using namespace cpattn;
-  if (desc == nullptr || acc == nullptr || k_blocks == nullptr || v_blocks == nullptr) return CPATTN_E_ARG;
-  const int chk = check_prefill(desc, rank, 0);
+  if (desc == nullptr || acc == nullptr || q_local == nullptr || k_blocks == nullptr || v_blocks == nullptr)
+    return CPATTN_E_ARG;
+  const int chk = check_prefill(desc, 0, 0);
   if (chk != CPATTN_OK) return chk;
   const int cp = desc->cp;
   if (link_workgroups < 0 || link_workgroups > kMaxLinkGroups) return CPATTN_E_ARG;
   if (cp > 1 && (k_recv == nullptr || v_recv == nullptr || n_recv < 2 || n_recv > kMaxRecv)) return CPATTN_E_ARG;
+  if (events == nullptr || n_events < 2 * cp) return CPATTN_E_ARG;
+  for (int e = 0; e < 2 * cp; ++e)
+    if (events[e] == nullptr) return CPATTN_E_ARG;
   const int64_t total = desc->num_seqs > 0 ? desc->cu_seqlens[desc->num_seqs] : 0;
   if (total == 0) return CPATTN_OK;
-  if (q_local == nullptr || acc->m == nullptr || acc->den == nullptr || acc->num == nullptr) return CPATTN_E_ARG;
-  if (k_blocks[rank] == nullptr || v_blocks[rank] == nullptr) return CPATTN_E_ARG;
+  const int fit = check_launches(desc);   // the ring-step launches below cannot fail validation
+  if (fit != CPATTN_OK) return fit;
+  for (int r = 0; r < cp; ++r) {
+    if (q_local[r] == nullptr || k_blocks[r] == nullptr || v_blocks[r] == nullptr) return CPATTN_E_ARG;
+    if (acc[r].m == nullptr || acc[r].den == nullptr || acc[r].num == nullptr) return CPATTN_E_ARG;
+  }
   const int64_t elem = desc->dtype == CPATTN_DT_BF16 ? 2 : 4;
   const int64_t block_bytes = local_rows(desc) * desc->n_kv * desc->head_dim * elem;
-  if (cp > 1) {
-    // every receive buffer is aligned, disjoint from every source block and from
-    // every other receive buffer
+  const int n_buf = cp > 1 ? cp * n_recv : 0;
+  // every receive buffer is aligned and disjoint from every block and from
+  // every other receive buffer
+  for (int x = 0; x < 2 * n_buf; ++x) {
+    void *const bx = x < n_buf ? k_recv[x] : v_recv[x - n_buf];
     for (int j = 0; j < cp; ++j)
-      for (int b = 0; b < n_recv; ++b)
-        if (validate_pass(k_blocks[j], k_recv[b], block_bytes, 1) != CPATTN_OK ||
-            validate_pass(k_blocks[j], v_recv[b], block_bytes, 1) != CPATTN_OK ||
-            validate_pass(v_blocks[j], k_recv[b], block_bytes, 1) != CPATTN_OK ||
-            validate_pass(v_blocks[j], v_recv[b], block_bytes, 1) != CPATTN_OK)
-          return CPATTN_E_ARG;
-    for (int x = 0; x < 2 * n_recv; ++x)
-      for (int y = x + 1; y < 2 * n_recv; ++y) {
-        void *const bx = x < n_recv ? k_recv[x] : v_recv[x - n_recv];
-        void *const by = y < n_recv ? k_recv[y] : v_recv[y - n_recv];
-        if (validate_pass(bx, by, block_bytes, 1) != CPATTN_OK) return CPATTN_E_ARG;
-      }
+      if (validate_pass(k_blocks[j], bx, block_bytes, 1) != CPATTN_OK ||
+          validate_pass(v_blocks[j], bx, block_bytes, 1) != CPATTN_OK)
+        return CPATTN_E_ARG;
+    for (int y = x + 1; y < 2 * n_buf; ++y) {
+      void *const by = y < n_buf ? k_recv[y] : v_recv[y - n_buf];
+      if (validate_pass(bx, by, block_bytes, 1) != CPATTN_OK) return CPATTN_E_ARG;
+    }
   }
-
-  Events comp(cp), comm(cp);
-  if (!comp.ok(cp) || !comm.ok(cp)) return CPATTN_E_DEVICE;
-  for (int i = 0; i < cp; ++i) {
-    // compute(i) on the block in hand: the rank's own at step 0, then the one
-    // transfer(i-1) delivered into receive buffer (i-1) % n_recv
-    if (i > 0 && hipStreamWaitEvent(compute, comm.e[i - 1], 0) != hipSuccess) return CPATTN_E_DEVICE;
-    const void *k = i == 0 ? k_blocks[rank] : k_recv[(i - 1) % n_recv];
-    const void *v = i == 0 ? v_blocks[rank] : v_recv[(i - 1) % n_recv];
-    const int rc = cpattn_ring_step_partial(desc, rank, i, q_local, k, v, acc, i > 0 ? 1 : 0, compute);
-    if (rc != CPATTN_OK) return rc;
-    if (hipEventRecord(comp.e[i], compute) != hipSuccess) return CPATTN_E_DEVICE;
-    if (i == cp - 1) break;
-    // transfer(i): the block of rank (rank - i - 1) mod cp into receive buffer
-    // i % n_recv, last read by compute(i + 1 - n_recv)
-    const int war = i + 1 - n_recv;
-    if (war >= 1 && hipStreamWaitEvent(transfer, comp.e[war], 0) != hipSuccess) return CPATTN_E_DEVICE;
-    const int src = ((rank - i - 1) % cp + cp) % cp;
-    if (launch_pass(k_blocks[src], k_recv[i % n_recv], block_bytes, link_workgroups, transfer) != hipSuccess ||
-        launch_pass(v_blocks[src], v_recv[i % n_recv], block_bytes, link_workgroups, transfer) != hipSuccess)
+  // events[0]: entry (compute stream); events[1 + i]: transfers of step i done;
+  // events[cp + i]: compute of step i done
+  hipEvent_t *const entry = events, *const comm = events + 1, *const comp = events + cp;
+  if (cp > 1) {
+    if (hipEventRecord(*entry, compute) != hipSuccess || hipStreamWaitEvent(transfer, *entry, 0) != hipSuccess)
       return CPATTN_E_DEVICE;
-    if (hipEventRecord(comm.e[i], transfer) != hipSuccess) return CPATTN_E_DEVICE;
+  }
+  for (int i = 0; i < cp; ++i) {
+    // compute(i): every rank on the block in hand, its own at step 0, then the
+    // one that transfer(i-1) delivered into its receive buffer (i-1) % n_recv
+    if (i > 0 && hipStreamWaitEvent(compute, comm[i - 1], 0) != hipSuccess) return CPATTN_E_DEVICE;
+    for (int r = 0; r < cp; ++r) {
+      const void *k = i == 0 ? k_blocks[r] : k_recv[r * n_recv + (i - 1) % n_recv];
+      const void *v = i == 0 ? v_blocks[r] : v_recv[r * n_recv + (i - 1) % n_recv];
+      const int rc = cpattn_ring_step_partial(desc, r, i, q_local[r], k, v, &acc[r], i > 0 ? 1 : 0, compute);
+      if (rc != CPATTN_OK) return rc;
+    }
+    if (i == cp - 1) break;
+    if (hipEventRecord(comp[i], compute) != hipSuccess) return CPATTN_E_DEVICE;
+    // transfer(i): rank r forwards the block in hand to rank r+1's receive
+    // buffer i % n_recv, which compute(i + 1 - n_recv) read last
+    const int war = i + 1 - n_recv;
+    if (war >= 1 && hipStreamWaitEvent(transfer, comp[war], 0) != hipSuccess) return CPATTN_E_DEVICE;
+    for (int r = 0; r < cp; ++r) {
+      const int to = (r + 1) % cp;
+      const void *k = i == 0 ? k_blocks[r] : k_recv[r * n_recv + (i - 1) % n_recv];
+      const void *v = i == 0 ? v_blocks[r] : v_recv[r * n_recv + (i - 1) % n_recv];
+      if (launch_pass(k, k_recv[to * n_recv + i % n_recv], block_bytes, link_workgroups, transfer) != hipSuccess ||
+          launch_pass(v, v_recv[to * n_recv + i % n_recv], block_bytes, link_workgroups, transfer) != hipSuccess)
+        return CPATTN_E_DEVICE;
+    }
+    if (hipEventRecord(comm[i], transfer) != hipSuccess) return CPATTN_E_DEVICE;
   }
   return CPATTN_OK;
 }

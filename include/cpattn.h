@@ -23,8 +23,9 @@
  *   - The caller owns all memory. Host pointers are read during the call
  *     only. Device pointers must stay valid until the work enqueued on the
  *     given stream has finished; the library keeps no pointer after it
- *     returns, allocates nothing and has no global state. Calls are
- *     reentrant. Faults of enqueued kernels surface at the caller's next
+ *     returns, allocates no memory (device or host) and creates no HIP
+ *     object (streams and events are the caller's), and has no global state.
+ *     Calls are reentrant. Faults of enqueued kernels surface at the caller's next
  *     synchronisation.
  *   - There are no defaults: cp, scale and the shapes are explicit (the
  *     spec's interface appendix: cp is an explicit positive integer, a
@@ -141,6 +142,16 @@ int cpattn_balanced_split(const int64_t *cu_seqlens, int32_t num_seqs, int32_t c
 int cpattn_balanced_split_padded(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t rank,
                                  int64_t *positions, int64_t *cu_local);
 
+/* Rows of one rank's local buffers (Q, K, V blocks and triples of a prefill
+ * description): sum over sequences of 2 * c_i, with c_i = L_i / (2*cp)
+ * (padded = 0; every L_i divisible by 2*cp) or ceil(L_i / (2*cp)) (padded = 1,
+ * pad rows included). Host only.
+ *   rows  out, HOST int64.
+ * Errors: E_ARG (null pointer, cp < 1, num_seqs < 0, padded not 0/1,
+ * cu_seqlens[0] != 0 or decreasing), E_DIVISIBILITY (padded = 0 and a length
+ * not divisible by 2*cp). */
+int cpattn_local_rows(const int64_t *cu_seqlens, int32_t num_seqs, int32_t cp, int32_t padded, int64_t *rows);
+
 /* One pass-KV ring step of one rank (Definitions table, "Pass-KV", "Ring step",
  * "Partial attention"). Computes, for every local query row of rank `rank`
  * and every query head, the causal partial attention over the KV block that
@@ -177,40 +188,55 @@ int cpattn_ring_step_partial(const cpattn_prefill_desc *desc, int32_t rank, int3
  * Errors: E_ARG, E_DEVICE. */
 int cpattn_ring_pass(const void *src, void *dst, int64_t bytes, int32_t workgroups, hipStream_t stream);
 
-/* The whole pass-KV ring of one rank with transfers overlapping compute
- * (Rationale: the ring's dependency contract; Acceptance, "overlap
- * effective"). For step i = 0 .. cp-1 it enqueues on `compute` the ring step
- * of cpattn_ring_step_partial (step 0 writes acc, later steps merge into it)
- * on the block in hand, and for i < cp-1 on `transfer` the cpattn_ring_pass
- * copies (K and V) that deliver the block of rank (rank - i - 1) mod cp for
- * step i+1 into receive buffer i % n_recv. Events carry exactly these edges:
- * compute(i) waits for transfer(i-1); transfer(i) follows transfer(i-1) and,
- * when i+1-n_recv >= 1, waits for compute(i+1-n_recv), which read the buffer
- * it overwrites (more buffers give a transfer more slack).
- * No edge runs from compute(i) to transfer(i): the two run concurrently.
- * When the call returns, all enqueued work is ordered before later work on
- * `compute` (compute(cp-1) waits for the last transfer).
- *   desc, rank, q_local  as for cpattn_ring_step_partial.
- *   k_blocks, v_blocks   HOST arrays of cp device pointers: the block each rank
- *                        holds ([S/cp, n_kv, head_dim], that rank's local
- *                        order); entry j stands for rank j's memory, read by
- *                        the transfers and, for j = rank, by step 0.
- *   k_recv, v_recv       HOST arrays of n_recv device pointers each: the receive
- *                        buffers, one block each, pairwise disjoint and disjoint
- *                        from the blocks (unused when cp = 1).
- *   n_recv               2 .. 16 when cp > 1.
- *   acc                  device triple for S/cp rows (written, then merged into).
- *   link_workgroups      `workgroups` of each transfer (0: copy engine), as for
- *                        cpattn_ring_pass.
- *   compute, transfer    streams; passing the same stream serialises the ring.
- * Errors: those of cpattn_ring_step_partial and cpattn_ring_pass, returned
- * before any work is enqueued; E_DEVICE if the runtime refuses an event or a
- * launch part-way. */
-int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, int32_t rank, const void *q_local,
+/* The whole pass-KV ring of the CP group, every rank emulated on this GPU, with
+ * the block transfers overlapping the compute (Definitions table, "Pass-KV" and
+ * "Ring step": each step a rank computes on the block in hand while forwarding
+ * it to its successor; Rationale: the ring's dependency contract; Acceptance,
+ * "overlap effective"). For step i = 0 .. cp-1 it enqueues on `compute` the ring
+ * steps of every rank r (cpattn_ring_step_partial on the block in hand: its own
+ * block at step 0, later the one received at step i-1; step 0 writes acc[r],
+ * later steps merge into it), and for i < cp-1 on `transfer` the copies
+ * (cpattn_ring_pass, K and V) by which every rank r forwards the block in hand
+ * to rank (r+1) mod cp's receive buffer i % n_recv. Rank r's block in hand at
+ * step i is therefore the block of rank (r - i) mod cp, as in
+ * cpattn_ring_step_partial. Events carry exactly these edges:
+ *   compute(i)  waits for transfer(i-1);
+ *   transfer(i) follows transfer(i-1) and, when i+1-n_recv >= 1, waits for
+ *               compute(i+1-n_recv), which read the buffers it overwrites;
+ *   transfer(0) waits for the work enqueued on `compute` before the call.
+ * No edge runs from compute(i) to transfer(i): the two run concurrently. When
+ * the call returns, all enqueued work is ordered before later work on `compute`
+ * (compute(cp-1) waits for the last transfer), so calls may follow one another
+ * on the same streams without a host synchronisation.
+ *   desc                  as for cpattn_ring_step_partial (rank and step are
+ *                         implied).
+ *   q_local               HOST array of cp device pointers: rank r's rows
+ *                         [R, n_hq, head_dim], R as for cpattn_ring_step_partial.
+ *   k_blocks, v_blocks    HOST arrays of cp device pointers: the block rank r
+ *                         holds, [R, n_kv, head_dim] in its local order; read only.
+ *   k_recv, v_recv        HOST arrays of cp * n_recv device pointers, rank-major
+ *                         (buffer b of rank r at r * n_recv + b), one block each,
+ *                         pairwise disjoint and disjoint from the blocks (unused
+ *                         when cp = 1).
+ *   n_recv                2 .. 16 when cp > 1.
+ *   acc                   HOST array of cp device triples for R rows each.
+ *   link_workgroups       `workgroups` of each transfer (0: copy engine), as for
+ *                         cpattn_ring_pass.
+ *   compute, transfer     streams; passing the same stream serialises the ring.
+ *   events, n_events      HOST array of n_events >= 2 * cp events created by the
+ *                         caller (hipEventCreateWithFlags; hipEventDisableTiming
+ *                         is enough), used to carry the edges above. The library
+ *                         records them and makes the streams wait on them; it
+ *                         creates and destroys none. They may be reused by the
+ *                         next call once this one has returned.
+ * Errors: those of cpattn_ring_step_partial and cpattn_ring_pass, E_ARG for a
+ * null event or n_events < 2 * cp, all returned before any work is enqueued;
+ * E_DEVICE if the runtime refuses an event or a launch part-way. */
+int cpattn_ring_prefill_overlapped(const cpattn_prefill_desc *desc, const void *const *q_local,
                                    const void *const *k_blocks, const void *const *v_blocks,
                                    void *const *k_recv, void *const *v_recv, int32_t n_recv,
                                    const cpattn_partial *acc, int32_t link_workgroups, hipStream_t compute,
-                                   hipStream_t transfer);
+                                   hipStream_t transfer, hipEvent_t *events, int32_t n_events);
 
 /* Merge and finalize (Definitions table, "Partial attention": the merge is
  * associative and order-independent).

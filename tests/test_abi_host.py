@@ -206,22 +206,28 @@ def test_ring_transfer_entry_points_reject_bad_arguments_without_gpu():
                         dtype=ca.DT_BF16, scale=0.125)
     block = 32 * 2 * 128 * 2            # S/cp rows x n_kv x head_dim x 2 bytes
     base = 1 << 24
-    kb = (vp * 2)(base, base + block)
-    vb = (vp * 2)(base + 2 * block, base + 3 * block)
-    kr = (vp * 2)(base + 4 * block, base + 5 * block)
-    vr = (vp * 2)(base + 6 * block, base + 7 * block)
+    at = lambda i: base + i * block
+    kb = (vp * 2)(at(0), at(1))
+    vb = (vp * 2)(at(2), at(3))
+    kr = (vp * 4)(at(4), at(5), at(6), at(7))        # cp * n_recv, rank-major
+    vr = (vp * 4)(at(8), at(9), at(10), at(11))
     n_recv = 2
-    part = ca._Partial(16, 16, 16)
-    q = vp(base + 8 * block)
+    parts = (ca._Partial * 2)(ca._Partial(16, 16, 16), ca._Partial(32, 32, 32))
+    qs = (vp * 2)(at(12), at(13))
+    ev = (vp * 4)(1, 2, 3, 4)             # stand-ins: every call below fails validation first
 
-    def call(desc=d, rank=0, k=kb, v=vb, krx=kr, vrx=vr, nr=n_recv, wg=4):
-        return lib.cpattn_ring_prefill_overlapped(ctypes.byref(desc), rank, q, k, v, krx, vrx, nr,
-                                                  ctypes.byref(part), wg, None, None)
-    assert call(rank=2) == ca.E_ARG
+    def call(desc=d, q=qs, k=kb, v=vb, krx=kr, vrx=vr, nr=n_recv, wg=4, events=ev, n_ev=4):
+        return lib.cpattn_ring_prefill_overlapped(ctypes.byref(desc), q, k, v, krx, vrx, nr, parts, wg, None, None,
+                                                  events, n_ev)
     assert call(wg=-1) == ca.E_ARG
     assert call(krx=None) == ca.E_ARG
     assert call(nr=1) == ca.E_ARG
     assert call(nr=17) == ca.E_ARG
+    assert call(q=None) == ca.E_ARG
+    assert call(q=(vp * 2)(at(12), None)) == ca.E_ARG
+    assert call(events=None) == ca.E_ARG
+    assert call(n_ev=3) == ca.E_ARG                         # fewer than 2 * cp events
+    assert call(events=(vp * 4)(1, 2, None, 4)) == ca.E_ARG
     bad = ca._PrefillDesc(cp=2, num_seqs=1, cu_seqlens=cu.ctypes.data_as(P), n_hq=4, n_kv=3, head_dim=128,
                           dtype=ca.DT_BF16, scale=0.125)
     assert call(desc=bad) == ca.E_DIVISIBILITY
@@ -229,10 +235,35 @@ def test_ring_transfer_entry_points_reject_bad_arguments_without_gpu():
                           dtype=ca.DT_BF16, scale=0.125)
     assert call(desc=bad) == ca.E_UNSUPPORTED
     # a receive buffer overlapping a source block, or another receive buffer
-    assert call(krx=(vp * 2)(base + block // 2, base + 5 * block)) == ca.E_ARG
-    assert call(vrx=(vp * 2)(base + 4 * block + 16, base + 7 * block)) == ca.E_ARG
+    assert call(krx=(vp * 4)(at(0) + block // 2, at(5), at(6), at(7))) == ca.E_ARG
+    assert call(vrx=(vp * 4)(at(8), at(9), at(10), at(7) + 16)) == ca.E_ARG
     # misaligned block
-    assert call(k=(vp * 2)(base + 8, base + block)) == ca.E_ARG
+    assert call(k=(vp * 2)(at(0) + 8, at(1))) == ca.E_ARG
+
+
+@pytest.mark.parametrize("lens,cp,padded", [([64, 128, 0], 2, 0), ([5, 13, 0, 1, 7], 2, 1), ([1000003], 8, 1),
+                                            ([12464, 15568, 14688, 9376, 15536, 16048], 4, 0)])
+def test_local_rows_matches_the_split(lens, cp, padded):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    split = oracle.balanced_split_padded if padded else oracle.balanced_split
+    want = split(cu, cp, 0)[0].size
+    assert ca.local_rows(cu, cp, bool(padded)) == want
+    for r in range(cp):
+        assert split(cu, cp, r)[0].size == want
+
+
+def test_local_rows_errors():
+    for args, code in ((([0, 6], 2, False), ca.E_DIVISIBILITY), (([0, 8, 4], 2, True), ca.E_ARG),
+                       (([0, 8], 0, False), ca.E_ARG), (([1, 8], 2, False), ca.E_ARG)):
+        with pytest.raises(ca.CpattnError) as e:
+            ca.local_rows(*args)
+        assert e.value.code == code, args
+    lib = ca.load()
+    out = ctypes.c_int64(0)
+    cu = np.array([0, 8], dtype=np.int64)
+    assert lib.cpattn_local_rows(cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1, 2, 2,
+                                 ctypes.byref(out)) == ca.E_ARG   # padded must be 0 or 1
+    assert lib.cpattn_local_rows(cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1, 2, 0, None) == ca.E_ARG
 
 
 @pytest.mark.parametrize("lens,cp", [([5, 13, 0, 1, 7], 2), ([3, 10, 6], 3), ([1, 2, 3, 4, 5, 6, 7, 8, 9], 8),
