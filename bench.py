@@ -244,6 +244,9 @@ def main():
                     help="skip the measurements of the other workloads that follow the timed steps")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the transfer/compute overlap measurements that follow the timed steps")
+    ap.add_argument("--config-only", choices=["gqa", "varlen", "mqa", "mla"], default=None,
+                    help="measure only this workload of the configs report (for profiling its kernels) and "
+                         "print its JSON; no headline step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -261,6 +264,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ca.load()
+    if args.config_only:
+        if args.config_only in ("gqa", "varlen"):
+            r = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS[args.config_only], reps=args.steps)
+        else:
+            heads = {"mqa": (32, 128), "mla": (128, 512)}[args.config_only]
+            r = _decode_gbs(ca, torch, 8, 1 << 20, 8, heads[0], 1, heads[1], reps=args.steps)
+        print(json.dumps({"config": args.config_only, **r}), flush=True)
+        return
     dev = "cuda"
     wp = synth.WORKLOADS["long"]
     wd = synth.WORKLOADS["decode"]

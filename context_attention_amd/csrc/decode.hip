@@ -606,13 +606,6 @@ struct Dec16Cfg<512> {
   static constexpr int TK = 32, NST = 2;
 };
 
-// Chunk permutation of a V tile for the transposed reads of this kernel: the
-// 16 rows one read touches land on distinct banks (checked for 32- and 64-bank
-// LDS).
-template <int D>
-__device__ __forceinline__ int v16_swizzle(int row) {
-  return (D == 64) ? 2 * ((row ^ (row >> 2)) & 1) + 4 * ((row >> 1) & 1) : 2 * (row & 7);
-}
 
 typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 

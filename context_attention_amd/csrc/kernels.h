@@ -38,6 +38,13 @@ __device__ __forceinline__ float max_across_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// max(x[lane], x[lane ^ 16]) in every lane: v_permlane16_swap exchanges the
+// odd and even 16-lane rows of a wave register to register.
+__device__ __forceinline__ float max_across_rows16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Element loads of an input row: 8 consecutive elements widened to fp32.
 template <typename T>
 struct Elem;

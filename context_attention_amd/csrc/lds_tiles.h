@@ -105,6 +105,58 @@ __device__ __forceinline__ bf16x8_t v_fragment(const __bf16 *Vc, int ks, int d0)
 #endif
 }
 
+// Chunk permutation of a V tile read by v16_fragment: the 16 rows one
+// transposed read of a wave touches land on distinct banks (checked for 32- and
+// 64-bank LDS).
+template <int W>
+__device__ __forceinline__ int v16_swizzle(int row) {
+  return (W == 64) ? 2 * ((row ^ (row >> 2)) & 1) + 4 * ((row >> 1) & 1) : 2 * (row & 7);
+}
+
+// The two transposed reads of v16_fragment at an address already computed
+// (element offset of the lane's first read; the second is 16 rows further on).
+template <int W>
+__device__ __forceinline__ bf16x8_t v16_read(const __bf16 *p0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const lds_i16x4 *p = (const lds_i16x4 *)p0;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * W));
+  const i16x4_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+#else
+  (void)p0;
+  return bf16x8_t{};
+#endif
+}
+
+// A operand of O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 for the 16 columns
+// [16 db, 16 db + 16) of a 32-key V tile with W columns per row (chunks placed
+// by v16_swizzle): lane (i = lane % 16, group gr = lane / 16) needs
+// V[4 gr + 0..3][16 db + i] (elements 0..3) and V[16 + 4 gr + 0..3][16 db + i]
+// (elements 4..7), the key order in which the S^T accumulators of two 16-key
+// blocks lay out the P fragment. Two ds_read_b64_tr_b16, lane j of a group
+// addressing row 4 gr + j / 4 at column 16 db + 4 (j % 4).
+template <int W>
+__device__ __forceinline__ bf16x8_t v16_fragment(const __bf16 *Vc, int db) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, gr = lane >> 4;
+  const int row = 4 * gr + (i >> 2);
+  const int cc = 16 * db + 4 * (i & 3);
+  const int off = row * W + 8 * ((cc >> 3) ^ v16_swizzle<W>(row)) + (cc & 7);   // rows +16 share the swizzle
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const lds_i16x4 *p = (const lds_i16x4 *)(Vc + off);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * W));
+  const i16x4_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
+#else
+  (void)Vc; (void)db;
+  return bf16x8_t{};
+#endif
+}
+
 // A 32 x 32 fp32 score tile of one wave in LDS, stored [quarter][lane] as
 // float4 so that every 16-byte access of a wave covers 1 KB of consecutive
 // banks.

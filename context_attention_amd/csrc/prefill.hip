@@ -22,7 +22,8 @@
 //       running sums) and shared by the 8 waves. S^T = K Q^T and O^T = V^T P^T run on
 //       v_mfma_f32_32x32x16_bf16, so every lane owns one query column of both
 //       products and the softmax needs a single cross-lane exchange per tile.
-//   ring_step_wide<HG>  bf16, head_dim 512: wave quads split d (below).
+//   ring_step_wide<HG>  bf16, head_dim 512: 16 query rows per wave over the
+//       whole of d on v_mfma_f32_16x16x32_bf16 (below).
 //   ring_step_generic<T, D>  fp32: one workgroup per (query row, query head),
 //       fp32 arithmetic throughout.
 #include "kernels.h"
@@ -98,7 +99,7 @@ struct Cfg<128> {
 template <>
 struct Cfg<512> {
   static constexpr int BN = 32, NW = 8, WPE = 2;
-  static constexpr int NS = 4;   // waves that share a 32-row block, each owning D / NS columns
+  static constexpr int RW = 16;  // query rows of a wave (the columns of v_mfma_f32_16x16x32_bf16)
 };
 template <int D>
 constexpr int kThreadsOf = 64 * Cfg<D>::NW;
@@ -107,7 +108,7 @@ constexpr int kThreadsOf = 64 * Cfg<D>::NW;
 template <int D, int HG>
 constexpr int kRowsMfma = 32 * Cfg<D>::NB * Cfg<D>::NW / HG;
 template <int HG>
-constexpr int kRowsWide = 32 * (Cfg<512>::NW / Cfg<512>::NS) / HG;
+constexpr int kRowsWide = Cfg<512>::RW * Cfg<512>::NW / HG;
 
 // Per-thread byte offsets (relative to the first key row of a tile) of the
 // buffer-to-LDS copies of a K and a V tile. Lane L of a wave writes bytes
@@ -289,6 +290,17 @@ struct TileWalk {
     return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, kBufferWord3};
   }
 };
+
+// Buffer resource of key row q of a tile (tile resource t, as from TileWalk or
+// tile_words), for the 1 KB of one head at byte gbase of the row: based there,
+// with 1 KB in range when the row holds a visible key (q * row_bytes below the
+// tile's range; ranges are whole rows, and a clamped range still covers the
+// 32 rows of a tile) and an empty range otherwise.
+__host__ __device__ __forceinline__ u32x4_t row_words(u32x4_t t, int q, uint32_t row_bytes, uint32_t gbase) {
+  const uint64_t base = ((uint64_t)(t[1] & 0xFFFFu) << 32 | t[0]) + (uint64_t)q * row_bytes + gbase;
+  const uint32_t nrec = (uint32_t)q * row_bytes < t[2] ? 1024u : 0u;
+  return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, t[3]};
+}
 
 template <int D, int HG>
 __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
@@ -606,42 +618,43 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// head_dim 512 (bf16): wave quads split d.
+// head_dim 512 (bf16): 16 query rows per wave over the whole of d.
 // ----------------------------------------------------------------------------
-// A workgroup of 8 waves (two per SIMD) is two groups of NS = 4; the waves of a
-// group own the same 32 query rows and a quarter of d each: Q and the output
-// accumulator of a wave cover its 128 columns (32 + 64 registers), which keeps
-// a wave within the 256 registers of two waves per SIMD. QK^T is split over d
-// too: each wave multiplies its quarter, the group exchanges the partial 32 x 32
-// score tiles through LDS and every wave adds the four in the same order, so all
-// hold bit-identical scores and run the same softmax; the PV product then fills
-// each wave's quarter of the output. Keys come in 32-key tiles copied straight
-// into double-buffered LDS (2 x 32 KB for K and for V, 32 KB of partial scores).
+// A workgroup of 8 waves (two per SIMD) holds HG query heads of one kv group x
+// 128 / HG query rows; wave w owns 16 rows of head w % HG. The rows are the 16
+// columns of v_mfma_f32_16x16x32_bf16 in both products, S^T = K Q^T (16-key
+// blocks x 16 rows, k-steps of 32 columns of d) and O^T = V^T P^T (16-column
+// blocks of d x 16 rows, the 32 keys of a tile as one k-step), so a wave keeps
+// its Q fragments (64 registers) and its whole output (128 registers) and no
+// score leaves the wave: the softmax needs two cross-lane exchanges per tile
+// and nothing goes through LDS but the K and V tiles. Lane l holds row l % 16;
+// its 16-lane group g holds keys 4g + {0..3} and 16 + 4g + {0..3} of a tile,
+// the order the P operand and the transposed reads of V^T share. 32-key K and V
+// tiles (32 KB each) are copied straight into double-buffered LDS (128 KB),
+// every 1 KB copy a whole key row; the copies of tile t+1 fly while tile t
+// computes, with one barrier per tile.
 template <int HG>
 __global__ __launch_bounds__(kThreadsOf<512>) __attribute__((amdgpu_waves_per_eu(Cfg<512>::WPE, Cfg<512>::WPE)))
 void ring_step_wide(SeqTable tab, StepArgs a) {
   constexpr int D = 512;
   constexpr int BN = Cfg<D>::BN;                // 32 keys per tile
-  constexpr int NS = Cfg<D>::NS;                // waves per row block
+  constexpr int NW = Cfg<D>::NW;
+  constexpr int RW = Cfg<D>::RW;                // 16 rows per wave
   constexpr int BM = kRowsWide<HG>;             // query rows per workgroup
-  constexpr int DW = D / NS;                    // columns of d per wave
-  constexpr int KSH = DW / 16;                  // QK^T k-steps over a wave's columns
-  constexpr int DBH = DW / 32;                  // output d blocks of a wave
-  constexpr int KSZ = BN * D;
-  constexpr int VSZ = BN * D;
+  constexpr int KS = D / 32;                    // QK^T k-steps
+  constexpr int DB = D / 16;                    // 16-column blocks of O^T
+  constexpr int TSZ = BN * D;                   // bf16 elements of a K (or V) tile
+  constexpr int CPW = BN / NW;                  // 1 KB key rows each wave copies per tile
+  static_assert(CPW * NW == BN, "a tile's key rows split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][KSZ];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][VSZ];
-  // partial scores, one 32 x 32 tile per wave, stored [wave][quarter][lane] so
-  // that every 16-byte access of a wave covers 1 KB of consecutive banks
-  __shared__ __attribute__((aligned(16))) f32x4_t Sx[Cfg<D>::NW][4][64];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][TSZ];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int qi = lane & 31;
-  const int hf = lane >> 5;
-  const int grp = wave / NS, dh = wave % NS;
+  const int col = lane & 15;     // the lane's query row within the wave's 16
+  const int grp = lane >> 4;     // 16-lane group
 
   const int n_hg = a.n_hq / HG;
   int unit, hg;
@@ -655,10 +668,10 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const int qa = tail ? a.a_tail : a.a_head;
   const int64_t qrow0 = tab.row_off[si] + (tail ? c : 0);
 
-  const int h = hg * HG + (grp % HG);
+  const int h = hg * HG + (wave % HG);
   const int rep = a.n_hq / a.n_kv;
   const int g = h / rep;
-  const int wrow0 = tile * BM + (grp / HG) * 32;
+  const int wrow0 = tile * BM + (wave / HG) * RW;           // wave's first row inside the chunk
   const int wg_row_end = min(c, tile * BM + BM);
 
   const int len = tab.len[si];
@@ -666,190 +679,191 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const Segs<BN> sg = make_segs<BN>(a, qa, c, len, tab.row_off[si], min(wg_row_end, q_valid));
   const int nseg = sg.nseg;
 
-  const int row = wrow0 + qi;
+  const int row = wrow0 + col;
   const bool row_in = row < c;          // a row of the local buffer
   const bool row_ok = row < q_valid;    // a real (non-pad) row
   const int64_t grow = qrow0 + row;
   float *mptr = a.m + (grow * a.n_hq + h);
   float *dptr = a.den + (grow * a.n_hq + h);
-  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D + dh * DW;
+  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D;
 
   if (nseg == 0) {
+    // every row of this workgroup sees no key: the identity (unchanged when accumulating)
     if (!a.accumulate && row_in) {
-      if (hf == 0 && dh == 0) store_stats(mptr, dptr, kNegInf, 0.f);
+      if (grp == 0) store_stats(mptr, dptr, kNegInf, 0.f);
 #pragma unroll
-      for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4_t *>(nptr + 16 * db + 4 * grp) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     return;
   }
   const int ntiles = sg.tiles();
 
-  // Q fragments of this wave's half of d
-  bf16x8_t qf[KSH];
-  {
-    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + (grow * a.n_hq + h) * (int64_t)D + dh * DW + 8 * hf;
+  const char *kblock = reinterpret_cast<const char *>(a.k);
+  const char *vblock = reinterpret_cast<const char *>(a.v);
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
+  // Copies: wave w copies key rows q = w + NW i (i < CPW) of a tile, each
+  // through a buffer resource of its own (row_words: based at the row's head,
+  // 1 KB in range when the row holds a visible key, else empty), so every lane
+  // offset stays below 1 KB. Lane L loads the 16 bytes that belong at position
+  // L of the swizzled LDS row, the logical chunk L ^ swizzle(q); with
+  // q = w + 8 i that is L ^ (w + 8 (i & 1)) for K and L ^ 2 w for V, so three
+  // lane offsets serve every copy.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  static_assert(NW == 8 && CPW % 2 == 0, "the copy offsets assume 8 waves");
+  const uint32_t koff0 = (uint32_t)((lane ^ k_swizzle<D>(wv)) * 16);
+  const uint32_t koff1 = (uint32_t)((lane ^ k_swizzle<D>(wv + 8)) * 16);
+  const uint32_t voff = (uint32_t)((lane ^ v16_swizzle<D>(wv)) * 16);
+  const uint32_t gbase = (uint32_t)(g * D * 2);
+  auto issue = [&](u32x4_t rk, u32x4_t rv, int buf) {
+    const u32x4_t sk = uniform_words(rk), sv = uniform_words(rv);
 #pragma unroll
-    for (int ks = 0; ks < KSH; ++ks)
-      qf[ks] = row_ok ? *reinterpret_cast<const bf16x8_t *>(qp + ks * 16)
+    for (int i = 0; i < CPW; ++i) {
+      const int q = wv + NW * i;
+      dma_1k((i & 1) ? koff1 : koff0, uniform_words(row_words(sk, q, row_bytes, gbase)), Ks[buf] + q * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int q = wv + NW * i;
+      dma_1k(voff, uniform_words(row_words(sv, q, row_bytes, gbase)), Vt[buf] + q * 512);
+    }
+  };
+  // LDS read offsets (elements). K (A operand of S^T = K Q^T, k-step ks =
+  // 4 m + j): row col, logical chunk 4 ks + grp, swizzled by col: chunk
+  // 4 (ks ^ (col >> 2)) + (grp ^ (col & 3)) = 16 m + 4 (j ^ (col >> 2)) + ...,
+  // so kbase[j] + 128 m, and 16 rows further for the second key block. V^T
+  // (16-column block db = 8 m + j, v16_fragment's addresses): vbase[j] + 128 m.
+  int kbase[4], vbase[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kbase[j] = col * D + 8 * (4 * (j ^ (col >> 2)) + (grp ^ (col & 3)));
+  {
+    const int vrow = 4 * grp + (col >> 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vbase[j] = vrow * D + 16 * (j ^ (vrow & 7)) + 8 * ((col >> 1) & 1) + 4 * (col & 1);
+  }
+
+  // tile 0 into buffer 0; the walks give the resources of tile 1 on
+  issue(tile_words(kblock, sg.row[0], sg.end[0], row_bytes), tile_words(vblock, sg.row[0], sg.end[0], row_bytes), 0);
+  TileWalk<BN> kw(sg, ntiles, kblock, 1, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds q[row][32 ks + 8 grp .. +8]
+  bf16x8_t qf[KS];
+  {
+    const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + (grow * a.n_hq + h) * (int64_t)D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = row_ok ? *reinterpret_cast<const bf16x8_t *>(qp + 32 * ks)
                       : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
   }
 
   const float sl2 = a.scale * kLog2e;
-  const float thr = kRescaleLog2 / sl2;
-  float m_ref = kNegInf;
-  float l_run = 0.f;
-  f32x16_t oacc[DBH];
+  const float thr = kRescaleLog2 / sl2;   // rescale threshold in raw-score units
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4_t oacc[DB];
 #pragma unroll
-  for (int db = 0; db < DBH; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-
-  const char *kblock = reinterpret_cast<const char *>(a.k);
-  const char *vblock = reinterpret_cast<const char *>(a.v);
-  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
-  const StageMap<D> smap = stage_map<D>(row_bytes, g);
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // partial S^T = K Q^T over this wave's half of d for the 32 keys of a tile
-  auto qk_half = [&](const __bf16 *Kc, f32x16_t &sp) {
-    const int key = qi;
-    sp = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < KSH; ++ks) {
-      const int ch = (dh * KSH + ks) * 2 + hf;
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Kc[key * D + ((ch ^ k_swizzle<D>(key)) * 8)]);
-      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sp, 0, 0, 0);
-    }
-  };
-
-  {
-    load_tile<D>(smap.k, tile_words(kblock, sg.row[0], sg.end[0], row_bytes), Ks[0]);
-    load_tile<D>(smap.v, tile_words(vblock, sg.row[0], sg.end[0], row_bytes), Vt[0]);
-    if (ntiles > 1) {
-      const int s1 = sg.seg(1), k1 = sg.k0(1);
-      load_tile<D>(smap.k, tile_words(kblock, sg.row[s1] + k1, sg.end[s1] - k1, row_bytes), Ks[1]);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  f32x16_t spart;
-  qk_half(Ks[0], spart);
-  put_scores(Sx[wave], spart);
-  __syncthreads();
-  // copy resources of K from tile 2 on and of V from tile 1 on; each iteration
-  // uses the pair computed at the end of the one before
-  TileWalk<BN> kw(sg, ntiles, kblock, 2, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
-  u32x4_t kd = kw.words(), vd = vw.words();
 
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
+    // this wave's copies of tile it have landed; after the barrier every
+    // wave's have, and every wave is done with tile it-1, whose buffer the
+    // copies of tile it+1 overwrite
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    issue(kw.words(), vw.words(), cur ^ 1);
+    kw.next();
+    vw.next();
+
     const int sc = sg.seg(it);
     const int k0 = sg.k0(it);
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    load_tile<D>(smap.k, kd, Ks[cur]);
-    load_tile<D>(smap.v, vd, Vt[cur ^ 1]);
-
-    // full scores of tile it: the group's partials summed in one fixed order
-    f32x16_t sacc = get_scores(Sx[grp * NS]);
+    // ---- S^T = K Q^T: key blocks 0..15 (s0) and 16..31 (s1) of the tile
+    const __bf16 *Kc = Ks[cur];
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 1; w < NS; ++w) sacc += get_scores(Sx[grp * NS + w]);
-    __syncthreads();   // both partials read before either is overwritten
-
+    for (int ks = 0; ks < KS; ++ks) {
+      const __bf16 *kp = Kc + kbase[ks & 3] + 128 * (ks >> 2);
+      const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(kp);
+      const bf16x8_t k1f = *reinterpret_cast<const bf16x8_t *>(kp + 16 * D);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0f, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1f, qf[ks], s1, 0, 0, 0);
+    }
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const bool vis = (kk < kend) && (!diag || kk <= row);
-        if (!vis) sacc[r] = kNegInf;
+      for (int t = 0; t < 4; ++t) {
+        const int kk0 = k0 + 4 * grp + t, kk1 = kk0 + 16;
+        if (!(kk0 < kend && (!diag || kk0 <= row))) s0[t] = kNegInf;
+        if (!(kk1 < kend && (!diag || kk1 <= row))) s1[t] = kNegInf;
       }
     }
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+
+    // ---- online softmax: the row's 32 keys lie in the 4 lanes col, col + 16, ...
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mx = max_across_rows16(mx);
     mx = max_across_halves(mx);
     if (__any(mx > m_ref + thr)) {
       const float m_new = fmaxf(m_ref, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       m_ref = m_new;
     }
     const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
-
-    qk_half(Ks[cur ^ 1], spart);   // next tile's partial scores
-    uint32_t pk[8];
+    uint32_t pk[4];
+    pk[0] = pack_bf16x2(exp2_fast(fmaf(s0[0], sl2, -mref)), exp2_fast(fmaf(s0[1], sl2, -mref)));
+    pk[1] = pack_bf16x2(exp2_fast(fmaf(s0[2], sl2, -mref)), exp2_fast(fmaf(s0[3], sl2, -mref)));
+    pk[2] = pack_bf16x2(exp2_fast(fmaf(s1[0], sl2, -mref)), exp2_fast(fmaf(s1[1], sl2, -mref)));
+    pk[3] = pack_bf16x2(exp2_fast(fmaf(s1[2], sl2, -mref)), exp2_fast(fmaf(s1[3], sl2, -mref)));
+    // denominator from the same rounded values the PV product uses
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(fmaf(sacc[r], sl2, -mref));
-      const float p1 = exp2_fast(fmaf(sacc[r + 1], sl2, -mref));
-      pk[r >> 1] = pack_bf16x2(p0, p1);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), ones, l_run, false);
-    }
+    for (int i = 0; i < 4; ++i)
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, l_run, false);
+    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+
+    // ---- O^T += V^T P^T: lane (d column col of block db, group grp) takes
+    // V[4 grp + 0..3][16 db + col] and V[16 + 4 grp + 0..3][16 db + col], two
+    // transposed reads
     const __bf16 *Vc = Vt[cur];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int base = ks * 4;
-      u32x4_t pw = {pk[base], pk[base + 1], pk[base + 2], pk[base + 3]};
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-      for (int db = 0; db < DBH; ++db) {
-        const int d0 = dh * DW + db * 32;
-        const bf16x8_t vf = v_fragment<D>(Vc, ks, d0);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
-      }
-    }
-
-    kw.next();
-    vw.next();
-    kd = kw.words();
-    vd = vw.words();
-    put_scores(Sx[wave], spart);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    for (int db = 0; db < DB; ++db)
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v16_read<D>(Vc + vbase[db & 7] + 128 * (db >> 3)), pf,
+                                                         oacc[db], 0, 0, 0);
   }
+  // the copies issued past the last tile (empty ranges: zeros, no memory read)
+  // land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // a pad row is stored as a row that saw no key (the merge identity)
-  const float l_sum = l_run + __shfl_xor(l_run, 32);
-  const float l_tot = row_ok ? l_sum : 0.f;
-  // all waves of a group read the old max and denominator; every wave reaches the
-  // barrier before one of them overwrites them
-  float m_old = kNegInf, d_old = 0.f;
-  if (a.accumulate && row_in) {
-    m_old = *mptr;
-    d_old = *dptr;
-  }
-  __syncthreads();
+  // ---- epilogue: natural-log max, full denominator, optional merge, store
+  // (the 4 groups hold disjoint keys of the row: their sums add up)
+  float l_sum = l_run + __shfl_xor(l_run, 16);
+  l_sum += __shfl_xor(l_sum, 32);
+  const float l_tot = row_ok ? l_sum : 0.f;   // a pad row is stored as a row that saw no key
   if (!row_in) return;
   const float m_nat = (m_ref == kNegInf || !row_ok) ? kNegInf : m_ref * a.scale;
-  float w_old = 0.f, w_new = 1.f, m_out = m_nat;
+  float w_old = 0.f, w_new = 1.f;
   if (a.accumulate) {
-    merge_weights(m_old, m_nat, m_out, w_old, w_new);
-    const float d_out = w_old * d_old + w_new * l_tot;
-    if (hf == 0 && dh == 0) store_stats(mptr, dptr, m_out, d_out);
-  } else if (hf == 0 && dh == 0) {
+    float m_out;
+    merge_weights(*mptr, m_nat, m_out, w_old, w_new);
+    const float d_out = w_old * (*dptr) + w_new * l_tot;
+    if (grp == 0) store_stats(mptr, dptr, m_out, d_out);
+  } else if (grp == 0) {
     store_stats(mptr, dptr, m_nat, l_tot);
   }
 #pragma unroll
-  for (int db = 0; db < DBH; ++db)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
-      f32x4_t o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
-      if (!row_ok) o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (a.accumulate) {
-        const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
-        o = old * w_old + o * w_new;
-      }
-      *reinterpret_cast<f32x4_t *>(p) = o;
+  for (int db = 0; db < DB; ++db) {
+    float *p = nptr + 16 * db + 4 * grp;
+    f32x4_t o = row_ok ? oacc[db] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (a.accumulate) {
+      const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
+      o = old * w_old + o * w_new;
     }
+    *reinterpret_cast<f32x4_t *>(p) = o;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -999,17 +1013,19 @@ hipError_t launch_wide(const SeqTable &t, const StepArgs &a, int units, hipStrea
   return hipGetLastError();
 }
 
-// heads per workgroup: up to 4 query heads of one kv group (2 for head_dim 512,
-// whose workgroup holds two wave quads)
+// heads per workgroup: up to 4 query heads of one kv group
 int pick_hg_d(int d, int rep) {
-  const int hg = pick_hg(rep);
-  return (d == 512 && hg > 2) ? 2 : hg;
+  (void)d;
+  return pick_hg(rep);
 }
 
 template <int D>
 hipError_t launch_mfma_d(const SeqTable &t, const StepArgs &a, int units, hipStream_t s) {
   if constexpr (D == 512) {
-    return pick_hg_d(512, a.n_hq / a.n_kv) == 2 ? launch_wide<2>(t, a, units, s) : launch_wide<1>(t, a, units, s);
+    const int hg = pick_hg_d(512, a.n_hq / a.n_kv);
+    if (hg == 4) return launch_wide<4>(t, a, units, s);
+    if (hg == 2) return launch_wide<2>(t, a, units, s);
+    return launch_wide<1>(t, a, units, s);
   } else {
     const int hg = pick_hg(a.n_hq / a.n_kv);
     if (hg == 4) return launch_mfma<D, 4>(t, a, units, s);
@@ -1037,7 +1053,10 @@ int rows_mfma(int hg) {
 // the head grouping launch_mfma_d picks
 int rows_per_unit(int dtype, int d, int rep) {
   if (!use_mfma(dtype, d)) return 1;
-  if (d == 512) return pick_hg_d(512, rep) == 2 ? kRowsWide<2> : kRowsWide<1>;
+  if (d == 512) {
+    const int hg = pick_hg_d(512, rep);
+    return hg == 4 ? kRowsWide<4> : hg == 2 ? kRowsWide<2> : kRowsWide<1>;
+  }
   const int hg = pick_hg(rep);
   return d == 64 ? rows_mfma<64>(hg) : rows_mfma<128>(hg);
 }

@@ -33,6 +33,42 @@ static void walk_cmp(const Segs<BN> &sg, int ntiles, const char *blk, uint32_t r
   }
 }
 
+// The per-row copy resources of the head_dim 512 kernel (row_words of the
+// walked tile resource), for every tile t0 .. past the end and every key row q
+// of a 32-key tile and every head offset: a row with keys in range reads the
+// 1 KB of one head inside a visible key row of the tile's segment (every lane
+// offset is below 1 KB); every visible key row of the tile is copied; rows past
+// the visible keys, and every row of a tile past the end, have an empty range.
+static long long rows_checked = 0;
+static void rows_cmp(const Segs<32> &sg, int ntiles, const char *blk, uint32_t rb, int n_kv) {
+  TileWalk<32> w(sg, ntiles, blk, 1, rb);
+  const uint64_t b0 = (uint64_t)(uintptr_t)blk;
+  for (int t = 1; t <= ntiles + 2; ++t, w.next()) {
+    const u32x4_t tw = w.words();
+    int vis = 0;
+    int64_t first = 0;
+    if (t < ntiles) {
+      const int s = sg.seg(t), k = sg.k0(t);
+      vis = std::min(32, sg.end[s] - k);
+      first = sg.row[s] + k;
+    }
+    for (int q = 0; q < 32; ++q)
+      for (int g = 0; g < n_kv; g += (n_kv > 4 ? n_kv / 4 : 1)) {
+        const uint32_t gbase = (uint32_t)g * 1024u;
+        const u32x4_t r = row_words(tw, q, rb, gbase);
+        ++rows_checked;
+        const uint64_t base = (uint64_t)(r[1] & 0xFFFFu) << 32 | r[0];
+        const bool want = q < vis;
+        const bool ok = want ? (r[2] == 1024u && base == b0 + (uint64_t)(first + q) * rb + gbase &&
+                                gbase + 1024u <= rb)
+                             : r[2] == 0u;
+        if (!ok && ++bad < 10)
+          printf("ROW MISMATCH t=%d q=%d g=%d vis=%d nrec=%u base=%llx\n", t, q, g, vis, r[2],
+                 (unsigned long long)base);
+      }
+  }
+}
+
 // every workgroup of one ring step, geometry as in the kernels
 template <int BN>
 static void launch_cmp(const std::vector<long long> &lens, int cp, int rank, int step, int bm, int n_kv, int d) {
@@ -68,6 +104,7 @@ static void launch_cmp(const std::vector<long long> &lens, int cp, int rank, int
     const int ntiles = sg.tiles();
     walk_cmp<BN>(sg, ntiles, blk, rb, 2, ntiles + 3);   // K: tiles 2 .. past the end
     walk_cmp<BN>(sg, ntiles, blk, rb, 1, ntiles + 3);   // V: tiles 1 ..
+    if constexpr (BN == 32) rows_cmp(sg, ntiles, blk, rb, n_kv);
   }
 }
 
@@ -109,10 +146,11 @@ int main() {
   configs<64>(32 * 8 / 4, 128);   // d64/128 kernel, 4 heads per workgroup
   configs<64>(32 * 8 / 2, 128);
   configs<64>(32 * 8 / 1, 64);
-  configs<32>(32 * 2 / 2, 512);   // d512 kernel
-  configs<32>(32 * 2 / 1, 512);
+  configs<32>(kRowsWide<1>, 512);   // d512 kernel: K and V walks both from tile 1
+  configs<32>(kRowsWide<2>, 512);
+  configs<32>(kRowsWide<4>, 512);
   random_segs<64>(20000);
   random_segs<32>(20000);
-  printf("checked %lld resources, %lld mismatches\n", checked, bad);
+  printf("checked %lld resources and %lld row resources, %lld mismatches\n", checked, rows_checked, bad);
   return bad != 0;
 }

@@ -85,15 +85,20 @@ def test_padded_ring_overlapped_equals_sequential():
                           scale=1.0 / np.sqrt(d), padded=True)
     local = _padded_locals(ca, cu, cp, [q, k, v])
     comp, xfer = torch.cuda.Stream(), torch.cuda.Stream()
+    seqs = []
     for r in range(cp):
         q_r = local[r][1][0]
         seq = ca.new_partial(desc.rows, n_hq, d)
         for t in range(cp):
             j = (r - t) % cp
             ca.ring_step_partial(desc, r, t, q_r, local[j][1][1], local[j][1][2], seq, accumulate=t > 0)
-        x = ca.overlap.make_inputs(desc, r, q_r, [l[1][1] for l in local], [l[1][2] for l in local])
-        torch.cuda.synchronize()
-        ca.ring_prefill_overlapped(desc, r, q_r, x.k_blocks, x.v_blocks, x.k_recv, x.v_recv, x.acc, 0, comp, xfer)
-        torch.cuda.synchronize()
-        for a, b in ((x.acc.m, seq.m), (x.acc.den, seq.den), (x.acc.num, seq.num)):
+        seqs.append(seq)
+    x = ca.overlap.make_inputs(desc, [l[1][0] for l in local], [l[1][1] for l in local],
+                               [l[1][2] for l in local])
+    torch.cuda.synchronize()
+    ca.ring_prefill_overlapped(desc, x.q, x.k_blocks, x.v_blocks, x.k_recv, x.v_recv, x.acc, 0, comp, xfer,
+                               events=x.events)
+    torch.cuda.synchronize()
+    for r in range(cp):
+        for a, b in ((x.acc[r].m, seqs[r].m), (x.acc[r].den, seqs[r].den), (x.acc[r].num, seqs[r].num)):
             assert torch.equal(a, b), f"rank {r}"
