@@ -21,7 +21,8 @@ import numpy as np
 __all__ = [
     "CpattnError", "Partial", "PrefillDesc", "DecodeDesc", "lib_path", "load",
     "balanced_split", "balanced_split_padded", "local_rows", "padded_rows", "ring_step_partial", "ring_pass",
-    "ring_prefill_overlapped", "merge", "tree_reduce", "passq_decode", "passq_workspace_bytes",
+    "ring_prefill_overlapped", "merge", "tree_reduce", "passq_decode", "passq_decode_noalloc",
+    "passq_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
     "account", "new_partial", "RingEvents",
 ]
 
@@ -32,10 +33,12 @@ OK, E_ARG, E_DIVISIBILITY, E_UNSUPPORTED, E_OVERFLOW, E_WORKSPACE, E_DEVICE = ra
 _ERR_NAMES = {1: "CPATTN_E_ARG", 2: "CPATTN_E_DIVISIBILITY", 3: "CPATTN_E_UNSUPPORTED",
               4: "CPATTN_E_OVERFLOW", 5: "CPATTN_E_WORKSPACE", 6: "CPATTN_E_DEVICE"}
 DT_F32, DT_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20    # CPATTN_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_local_rows", "cpattn_ring_step_partial",
            "cpattn_ring_pass",
            "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_tree_reduce", "cpattn_passq_decode",
+           "cpattn_passq_decode_noalloc",
            "cpattn_account", "cpattn_version"]
 
 
@@ -113,6 +116,8 @@ def load():
     lib.cpattn_passq_decode.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp,
                                         ctypes.POINTER(ctypes.c_size_t), vp]
+    lib.cpattn_passq_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
+                                                ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp]
     lib.cpattn_account.argtypes = [ctypes.POINTER(_AccountIn), ctypes.POINTER(_AccountOut)]
     lib.cpattn_version.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -449,12 +454,8 @@ def passq_workspace_bytes(desc: DecodeDesc) -> int:
     return int(n.value)
 
 
-def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, shard_partials: Partial,
-                 out, lse, ws=None, stream=None) -> None:
-    """cpattn_passq_decode (see include/cpattn.h). Allocates the workspace with
-    torch when `ws` is None."""
-    import torch
-    lib = load()
+def _check_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, shard_partials: Partial,
+                  out, lse) -> None:
     b, hq, hd = desc.batch, desc.n_hq, desc.head_dim
     if tuple(q.shape) != (b, hq, hd):
         raise ValueError("q shape mismatch")
@@ -474,6 +475,15 @@ def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, sh
         _dev_check(t, desc.dtype)
     _dev_check(out, "f32")
     _dev_check(lse, "f32")
+
+
+def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, shard_partials: Partial,
+                 out, lse, ws=None, stream=None) -> None:
+    """cpattn_passq_decode (see include/cpattn.h). Allocates the workspace with
+    torch when `ws` is None."""
+    import torch
+    lib = load()
+    _check_decode(desc, q, k_shards, v_shards, shard_partials, out, lse)
     need = passq_workspace_bytes(desc)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -487,6 +497,22 @@ def passq_decode(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, sh
     _check(lib.cpattn_passq_decode(ctypes.byref(d), q.data_ptr(), ks, vs, ctypes.byref(sp), out.data_ptr(),
                                    lse.data_ptr(), ws.data_ptr(), ctypes.byref(n), _stream(stream)),
            "cpattn_passq_decode")
+
+
+def passq_decode_noalloc(desc: DecodeDesc, q, k_shards: Sequence, v_shards: Sequence, shard_partials: Partial,
+                         out, lse, stream=None) -> None:
+    """cpattn_passq_decode_noalloc (see include/cpattn.h): pass-Q decode with
+    the workspace in the library's per-GPU scratch buffer; nothing is
+    allocated."""
+    lib = load()
+    _check_decode(desc, q, k_shards, v_shards, shard_partials, out, lse)
+    d = desc._c()
+    ks = (ctypes.c_void_p * desc.cp)(*[t.data_ptr() for t in k_shards])
+    vs = (ctypes.c_void_p * desc.cp)(*[t.data_ptr() for t in v_shards])
+    sp = shard_partials._c()
+    _check(lib.cpattn_passq_decode_noalloc(ctypes.byref(d), q.data_ptr(), ks, vs, ctypes.byref(sp),
+                                           out.data_ptr(), lse.data_ptr(), _stream(stream)),
+           "cpattn_passq_decode_noalloc")
 
 
 def version() -> str:

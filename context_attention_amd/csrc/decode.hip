@@ -17,6 +17,8 @@
 // decode_reduce<D>: one workgroup per (batch entry, query head): folds the
 //   key splits into the per-shard triples (the partial that rank s would send),
 //   then reduces the cp shard triples into out and lse.
+#include <mutex>
+
 #include "kernels.h"
 #include "lds_tiles.h"
 
@@ -1025,13 +1027,11 @@ hipError_t launch_mfma(const MfmaArgs &a, int D, int64_t blocks, hipStream_t s) 
   return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace cpattn
-
-extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q, const void *const *k_shards,
-                                   const void *const *v_shards, const cpattn_partial *shard_partials, float *out,
-                                   float *lse, void *ws, size_t *ws_bytes, hipStream_t stream) {
-  using namespace cpattn;
+// The pass-Q decode of cpattn_passq_decode with the workspace given (ws ==
+// nullptr: only the size is stored).
+int passq_decode(const cpattn_decode_desc *desc, const void *q, const void *const *k_shards,
+                 const void *const *v_shards, const cpattn_partial *shard_partials, float *out, float *lse, void *ws,
+                 size_t *ws_bytes, hipStream_t stream) {
   if (desc == nullptr || ws_bytes == nullptr) return CPATTN_E_ARG;
   const cpattn_decode_desc d = *desc;
   if (d.cp < 1 || d.batch < 0 || d.kv_len < 0 || d.n_hq < 1 || d.n_kv < 1) return CPATTN_E_ARG;
@@ -1136,4 +1136,62 @@ extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q
   else hipLaunchKernelGGL(decode_reduce<512>, dim3(rb), rt, 0, stream, r);
   if (hipGetLastError() != hipSuccess) return CPATTN_E_DEVICE;
   return CPATTN_OK;
+}
+
+}  // namespace
+}  // namespace cpattn
+
+extern "C" int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q, const void *const *k_shards,
+                                   const void *const *v_shards, const cpattn_partial *shard_partials, float *out,
+                                   float *lse, void *ws, size_t *ws_bytes, hipStream_t stream) {
+  return cpattn::passq_decode(desc, q, k_shards, v_shards, shard_partials, out, lse, ws, ws_bytes, stream);
+}
+
+// ----------------------------------------------------------------------------
+// Pass-Q decode without allocation: the split triples live in a file-scope
+// device array instead of a caller's workspace. Each GPU holds its own copy of
+// the array from the module's load until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress returns for the current device
+// (the array's name is a host-side stand-in, not a device address).
+// ----------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[CPATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device; nullptr when the runtime cannot give it.
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" int cpattn_passq_decode_noalloc(const cpattn_decode_desc *desc, const void *q,
+                                           const void *const *k_shards, const void *const *v_shards,
+                                           const cpattn_partial *shard_partials, float *out, float *lse,
+                                           hipStream_t stream) {
+  // the split triples need no clearing: every (shard, batch entry, head, split)
+  // triple is written by the partial kernel before the reduction reads it
+  size_t need = 0;
+  const int rc = cpattn::passq_decode(desc, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &need,
+                                      stream);
+  if (rc != CPATTN_OK) return rc;
+  if (need > (size_t)CPATTN_NOALLOC_SCRATCH_BYTES) return CPATTN_E_WORKSPACE;
+  void *ws = scratch_address();
+  if (ws == nullptr) return CPATTN_E_DEVICE;
+  size_t have = (size_t)CPATTN_NOALLOC_SCRATCH_BYTES;
+  return cpattn::passq_decode(desc, q, k_shards, v_shards, shard_partials, out, lse, ws, &have, stream);
 }

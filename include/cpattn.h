@@ -290,6 +290,32 @@ int cpattn_passq_decode(const cpattn_decode_desc *desc, const void *q,
                         const cpattn_partial *shard_partials, float *out, float *lse,
                         void *ws, size_t *ws_bytes, hipStream_t stream);
 
+/* Size of the scratch buffer of cpattn_passq_decode_noalloc, in bytes (32 MiB). */
+#define CPATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Pass-Q decode that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The same computation, kernels and results as
+ * cpattn_passq_decode (bit for bit), with its workspace taken from a scratch
+ * buffer of CPATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on, from the module's load until the process ends; its address on the
+ * current device is looked up once, on the first call there. The call makes no
+ * allocation of its own (no hipMalloc, hipFree or allocating library routine).
+ *   arguments  as for cpattn_passq_decode, without ws / ws_bytes.
+ * Every call on a GPU uses that GPU's one scratch buffer: calls that may run at
+ * the same time on one GPU (from several streams or threads) race and must be
+ * ordered by the caller. Nothing in the buffer needs clearing between calls.
+ * Errors: those of cpattn_passq_decode; E_WORKSPACE when the description needs
+ * more than CPATTN_NOALLOC_SCRATCH_BYTES of workspace (the size
+ * cpattn_passq_decode reports with ws == NULL), returned before any device
+ * call; E_DEVICE when the runtime cannot give the buffer's address. This entry
+ * point keeps per-device state (the buffer and its looked-up address), unlike
+ * the others. */
+int cpattn_passq_decode_noalloc(const cpattn_decode_desc *desc, const void *q,
+                                const void *const *k_shards, const void *const *v_shards,
+                                const cpattn_partial *shard_partials, float *out, float *lse,
+                                hipStream_t stream);
+
 /* Inputs of cpattn_account. Prefill fields are used when cu_seqlens != NULL,
  * decode fields when kv_len > 0.
  *   cp, n_hq, n_kv, head_dim  as above; dtype_bytes = s, the model element size.

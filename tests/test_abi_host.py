@@ -302,3 +302,18 @@ def test_tree_reduce_rejects_bad_arguments_without_gpu():
     nul = (P * 2)(a, P(0, 65536, 131072))
     assert lib.cpattn_tree_reduce(4, 2, 128, nul, 2, None, None, None) == ca.E_ARG
     assert lib.cpattn_tree_reduce(0, 2, 128, arr, 2, None, None, None) == ca.OK
+
+
+def test_noalloc_decode_rejects_before_any_device_call():
+    """cpattn_passq_decode_noalloc validates the description and compares the
+    workspace it needs with its scratch buffer before touching the device."""
+    lib = ca.load()
+    big = ca._DecodeDesc(batch=8, cp=8, kv_len=1 << 20, n_hq=128, n_kv=1, head_dim=512, dtype=ca.DT_BF16,
+                         scale=0.04)
+    assert lib.cpattn_passq_decode_noalloc(ctypes.byref(big), None, None, None, None, None, None,
+                                           None) == ca.E_WORKSPACE
+    bad = ca._DecodeDesc(batch=8, cp=3, kv_len=1 << 20, n_hq=32, n_kv=8, head_dim=128, dtype=ca.DT_BF16,
+                         scale=0.04)
+    assert lib.cpattn_passq_decode_noalloc(ctypes.byref(bad), None, None, None, None, None, None,
+                                           None) == ca.E_DIVISIBILITY
+    assert lib.cpattn_passq_decode_noalloc(None, None, None, None, None, None, None, None) == ca.E_ARG
