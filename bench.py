@@ -75,6 +75,101 @@ def cpu_baseline_prefill(w, rows=64, target_s=15.0):
             "seconds": dt}
 
 
+def cpu_baseline_configs():
+    """The oracle (fp64 numpy, the same code the parity tests use) timed beside
+    the other workloads, each on the unit of work the GPU figure is quoted on
+    or a bounded sample of it:
+      tiny     the full problem: every rank's ring (partials and merges), the
+               unsplit two-pass reference and the pure-Python brute force;
+      gqa      one ring-step partial in full: rank 0 at step 1 (its 2048
+               tail-chunk rows x 32 heads against rank 7's block of 4096 keys,
+               all visible; the head-chunk rows see no key);
+      decode   one (batch entry, kv head, shard): 4 query heads against 131072
+               keys; the full decode (8 x 8 x 8 such units) is extrapolated;
+      varlen   rank 0 at step 1 of the wide-head workload on a sample: the
+               tail-chunk rows of every sequence that fall on every 16th row,
+               8 of the 64 heads, against the block of rank 3; the full call is
+               extrapolated by exact FLOPs.
+    Extrapolated times are labelled as such."""
+    import oracle
+    import synth
+    out = {}
+    perf = time.perf_counter
+    # ---- tiny: everything
+    w = synth.WORKLOADS["tiny"]
+    S = w.total_tokens
+    q, k, v = (synth.tensor_np(w.seed, t, (S, w.n_hq, w.head_dim), w.scale_in, w.dtype)
+               for t in (synth.TENSOR_Q, synth.TENSOR_K, synth.TENSOR_V))
+    t0 = perf()
+    oracle.ring_prefill(q, k, v, w.cu_seqlens, w.cp, w.softmax_scale)
+    t1 = perf()
+    oracle.attention_reference(q, k, v, w.cu_seqlens, w.softmax_scale)
+    t2 = perf()
+    oracle.brute_force_attention(q, k, v, w.cu_seqlens, w.softmax_scale)
+    t3 = perf()
+    out["tiny_prefill"] = {"sample": "the full problem", "ring_s": round(t1 - t0, 4),
+                           "reference_s": round(t2 - t1, 4), "brute_force_s": round(t3 - t2, 3)}
+    # ---- gqa: rank 0, step 1, in full
+    w = synth.WORKLOADS["gqa"]
+    S, cp, H, G, d = w.total_tokens, w.cp, w.n_hq, w.n_kv, w.head_dim
+    c = S // (2 * cp)
+    qs = synth.tensor_np(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, row_start=(2 * cp - 1) * c, rows=c)
+    kb = synth.tensor_np(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, row_start=(cp - 1) * c, rows=2 * c)
+    vb = synth.tensor_np(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, row_start=(cp - 1) * c, rows=2 * c)
+    t0 = perf()
+    oracle.partial_attention(qs, kb, vb, np.arange(c), np.arange(2 * c), None, w.softmax_scale, causal=False)
+    dt = perf() - t0
+    flops = 4 * d * H * c * 2 * c
+    out["gqa_prefill"] = {"sample": f"one ring-step partial in full (rank 0, step 1: {c} rows x {H} heads x {2 * c} keys)",
+                          "seconds": round(dt, 3), "flops": flops, "gflop_per_s": round(flops / dt / 1e9, 2)}
+    # ---- decode: one (batch entry, kv head, shard), extrapolated
+    w = synth.WORKLOADS["decode"]
+    b, Sd, dcp, H, G, d = w.batch, w.kv_len, w.cp, w.n_hq, w.n_kv, w.head_dim
+    n = Sd // dcp
+    rep = H // G
+    qd = synth.tensor_np(w.seed, synth.TENSOR_Q, (b, H, d), w.scale_in, w.dtype)[:1, :rep]
+    kd = synth.head_slice_np(w.seed, synth.TENSOR_K, (b * Sd, G, d), 0, w.scale_in, w.dtype, row_start=0, rows=n)
+    vd = synth.head_slice_np(w.seed, synth.TENSOR_V, (b * Sd, G, d), 0, w.scale_in, w.dtype, row_start=0, rows=n)
+    t0 = perf()
+    oracle.passq_decode(qd, kd[None], vd[None], 1, w.softmax_scale)
+    dt = perf() - t0
+    units = b * G * dcp
+    kv_bytes = 2 * n * d * 2
+    out["pass_q_decode"] = {"sample": f"one (batch entry, kv head, shard): {rep} query heads x {n} keys; "
+                                      f"the full decode is {units} such units",
+                            "seconds": round(dt, 3), "kv_gb_per_s": round(kv_bytes / dt / 1e9, 3),
+                            "extrapolated_full_s": round(dt * units, 1)}
+    # ---- varlen: rank 0, step 1, sampled rows and heads, extrapolated
+    w = synth.WORKLOADS["varlen"]
+    cp, H, d = w.cp, w.n_hq, w.head_dim
+    heads = list(range(0, H, 8))
+    cu = w.cu_seqlens
+    t_sum, f_sum, f_full = 0.0, 0, 0
+    for i, L in enumerate(w.seqlens):
+        c = L // (2 * cp)
+        start = int(cu[i])
+        rows = np.arange((2 * cp - 1) * c, 2 * cp * c, 16)
+        f_full += 4 * d * H * c * 2 * c
+        for hh in heads:
+            qh = synth.values_at_np(w.seed, synth.TENSOR_Q, ((start + rows)[:, None] * H + hh) * d
+                                    + np.arange(d)[None, :], w.scale_in, w.dtype)[:, None, :]
+            kh = synth.head_slice_np(w.seed, synth.TENSOR_K, (w.total_tokens, H, d), hh, w.scale_in, w.dtype,
+                                     row_start=start + (cp - 1) * c, rows=2 * c)
+            vh = synth.head_slice_np(w.seed, synth.TENSOR_V, (w.total_tokens, H, d), hh, w.scale_in, w.dtype,
+                                     row_start=start + (cp - 1) * c, rows=2 * c)
+            t0 = perf()
+            oracle.partial_attention(qh, kh, vh, np.arange(rows.size), np.arange(2 * c), None, w.softmax_scale,
+                                     causal=False)
+            t_sum += perf() - t0
+            f_sum += 4 * d * rows.size * 2 * c
+    out["wide_varlen_prefill"] = {"sample": f"rank 0, step 1: every 16th tail-chunk row of each sequence, heads "
+                                            f"{heads[0]}, {heads[1]}, ... ({len(heads)} of {H}) against rank 3's block",
+                                  "seconds": round(t_sum, 3), "flops": f_sum,
+                                  "gflop_per_s": round(f_sum / t_sum / 1e9, 2),
+                                  "extrapolated_call_s": round(t_sum * f_full / f_sum, 1)}
+    return out
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel sources changed since it was taken."""
@@ -423,6 +518,8 @@ def main():
         log("bench: timing the oracle on the CPU")
         cb = cpu_baseline_prefill(wp)
         cb.pop("seconds")
+        log("bench: timing the oracle beside the other workloads")
+        cb["configs"] = cpu_baseline_configs()
         res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 

@@ -291,16 +291,45 @@ struct TileWalk {
   }
 };
 
-// Buffer resource of key row q of a tile (tile resource t, as from TileWalk or
-// tile_words), for the 1 KB of one head at byte gbase of the row: based there,
-// with 1 KB in range when the row holds a visible key (q * row_bytes below the
-// tile's range; ranges are whole rows, and a clamped range still covers the
-// 32 rows of a tile) and an empty range otherwise.
-__host__ __device__ __forceinline__ u32x4_t row_words(u32x4_t t, int q, uint32_t row_bytes, uint32_t gbase) {
-  const uint64_t base = ((uint64_t)(t[1] & 0xFFFFu) << 32 | t[0]) + (uint64_t)q * row_bytes + gbase;
-  const uint32_t nrec = (uint32_t)q * row_bytes < t[2] ? 1024u : 0u;
-  return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, nrec, t[3]};
-}
+// The copy resources of the head_dim 512 kernel, one per key row of a tile,
+// walked tile by tile in scalar registers: for tile t (t0, t0 + 1, ...) and key
+// row q, the 1 KB of one head at byte gbase of the row, based there with 1 KB
+// in range when the row holds a visible key, and otherwise (rows past the
+// segment's visible keys, tiles past the last) an empty range at the block
+// start (the copy then writes zeros and touches no memory).
+template <int BN>
+struct RowWalk {
+  int t, n0, ntiles;
+  uint64_t blk;
+  uint64_t addr, addr1;    // first key row of tile t; of the second segment's first tile
+  int left, left1;         // visible keys from there to the segment's end
+  uint32_t step;           // bytes of one tile
+  __host__ __device__ __forceinline__ RowWalk(const Segs<BN> &sg, int ntiles_, const char *blk_, int t0, uint32_t rb)
+      : t(t0), n0(sg.n0), ntiles(ntiles_), blk((uint64_t)(uintptr_t)blk_) {
+    const int s = sg.seg(t0), k = sg.k0(t0);
+    addr = blk + (uint64_t)((sg.row[s] + k) * (int64_t)rb);
+    left = sg.end[s] - k;
+    addr1 = blk + (uint64_t)(sg.row[1] * (int64_t)rb);
+    left1 = sg.end[1];
+    step = (uint32_t)BN * rb;
+  }
+  __host__ __device__ __forceinline__ void next() {
+    ++t;
+    if (t == n0) {
+      addr = addr1;
+      left = left1;
+    } else {
+      addr += step;
+      left -= BN;
+    }
+  }
+  // q * rb + gbase fits 32 bits: the ring step rejects rows of 2^25 bytes or more
+  __host__ __device__ __forceinline__ u32x4_t row(int q, uint32_t rb, uint32_t gbase) const {
+    const bool ok = t < ntiles && q < left;
+    const uint64_t base = ok ? addr + (uint32_t)((uint32_t)q * rb + gbase) : blk;
+    return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, ok ? 1024u : 0u, kBufferWord3};
+  }
+};
 
 template <int D, int HG>
 __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(Cfg<D>::WPE, Cfg<D>::WPE)))
@@ -651,7 +680,9 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 Vt[2][TSZ];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // the wave index as a scalar: head, rows and copy addresses derived from it
+  // stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;     // the lane's query row within the wave's 16
   const int grp = lane >> 4;     // 16-lane group
@@ -683,11 +714,11 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const bool row_in = row < c;          // a row of the local buffer
   const bool row_ok = row < q_valid;    // a real (non-pad) row
   const int64_t grow = qrow0 + row;
-  float *mptr = a.m + (grow * a.n_hq + h);
-  float *dptr = a.den + (grow * a.n_hq + h);
-  float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D;
 
   if (nseg == 0) {
+    float *mptr = a.m + (grow * a.n_hq + h);
+    float *dptr = a.den + (grow * a.n_hq + h);
+    float *nptr = a.num + (grow * a.n_hq + h) * (int64_t)D;
     // every row of this workgroup sees no key: the identity (unchanged when accumulating)
     if (!a.accumulate && row_in) {
       if (grp == 0) store_stats(mptr, dptr, kNegInf, 0.f);
@@ -703,49 +734,53 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const char *vblock = reinterpret_cast<const char *>(a.v);
   const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
   // Copies: wave w copies key rows q = w + NW i (i < CPW) of a tile, each
-  // through a buffer resource of its own (row_words: based at the row's head,
-  // 1 KB in range when the row holds a visible key, else empty), so every lane
+  // through a buffer resource of its own (RowWalk: based at the row's head, 1 KB
+  // in range when the row holds a visible key, else empty), so every lane
   // offset stays below 1 KB. Lane L loads the 16 bytes that belong at position
   // L of the swizzled LDS row, the logical chunk L ^ swizzle(q); with
   // q = w + 8 i that is L ^ (w + 8 (i & 1)) for K and L ^ 2 w for V, so three
   // lane offsets serve every copy.
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = wave;
   static_assert(NW == 8 && CPW % 2 == 0, "the copy offsets assume 8 waves");
   const uint32_t koff0 = (uint32_t)((lane ^ k_swizzle<D>(wv)) * 16);
   const uint32_t koff1 = (uint32_t)((lane ^ k_swizzle<D>(wv + 8)) * 16);
   const uint32_t voff = (uint32_t)((lane ^ v16_swizzle<D>(wv)) * 16);
   const uint32_t gbase = (uint32_t)(g * D * 2);
-  auto issue = [&](u32x4_t rk, u32x4_t rv, int buf) {
-    const u32x4_t sk = uniform_words(rk), sv = uniform_words(rv);
+  auto issue = [&](const RowWalk<BN> &kw, const RowWalk<BN> &vw, int buf) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int q = wv + NW * i;
-      dma_1k((i & 1) ? koff1 : koff0, uniform_words(row_words(sk, q, row_bytes, gbase)), Ks[buf] + q * 512);
+      dma_1k((i & 1) ? koff1 : koff0, uniform_words(kw.row(q, row_bytes, gbase)), Ks[buf] + q * 512);
     }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const int q = wv + NW * i;
-      dma_1k(voff, uniform_words(row_words(sv, q, row_bytes, gbase)), Vt[buf] + q * 512);
+      dma_1k(voff, uniform_words(vw.row(q, row_bytes, gbase)), Vt[buf] + q * 512);
     }
   };
-  // LDS read offsets (elements). K (A operand of S^T = K Q^T, k-step ks =
-  // 4 m + j): row col, logical chunk 4 ks + grp, swizzled by col: chunk
+  // LDS read addresses. K (A operand of S^T = K Q^T, k-step ks = 4 m + j):
+  // row col, logical chunk 4 ks + grp, swizzled by col: chunk
   // 4 (ks ^ (col >> 2)) + (grp ^ (col & 3)) = 16 m + 4 (j ^ (col >> 2)) + ...,
-  // so kbase[j] + 128 m, and 16 rows further for the second key block. V^T
-  // (16-column block db = 8 m + j, v16_fragment's addresses): vbase[j] + 128 m.
-  int kbase[4], vbase[8];
+  // so kp[j] + 128 m, and 16 rows further for the second key block. V^T
+  // (16-column block db = 8 m + j, v16_fragment's addresses): vp[j] + 128 m.
+  // With the buffer index a constant (the loop below handles two tiles per
+  // iteration) every read is one of these 12 registers plus an immediate.
+  const __bf16 *kp[4];
+  const __bf16 *vp[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kbase[j] = col * D + 8 * (4 * (j ^ (col >> 2)) + (grp ^ (col & 3)));
+  for (int j = 0; j < 4; ++j) kp[j] = &Ks[0][col * D + 8 * (4 * (j ^ (col >> 2)) + (grp ^ (col & 3)))];
   {
     const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      vbase[j] = vrow * D + 16 * (j ^ (vrow & 7)) + 8 * ((col >> 1) & 1) + 4 * (col & 1);
+      vp[j] = &Vt[0][vrow * D + 16 * (j ^ (vrow & 7)) + 8 * ((col >> 1) & 1) + 4 * (col & 1)];
   }
 
-  // tile 0 into buffer 0; the walks give the resources of tile 1 on
-  issue(tile_words(kblock, sg.row[0], sg.end[0], row_bytes), tile_words(vblock, sg.row[0], sg.end[0], row_bytes), 0);
-  TileWalk<BN> kw(sg, ntiles, kblock, 1, row_bytes), vw(sg, ntiles, vblock, 1, row_bytes);
+  // tile 0 into buffer 0, then the walks move on to tile 1
+  RowWalk<BN> kw(sg, ntiles, kblock, 0, row_bytes), vw(sg, ntiles, vblock, 0, row_bytes);
+  issue(kw, vw, 0);
+  kw.next();
+  vw.next();
 
   // Q fragments (B operand of S^T = K Q^T): lane holds q[row][32 ks + 8 grp .. +8]
   bf16x8_t qf[KS];
@@ -765,14 +800,14 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
+  // one tile in buffer `cur` (a constant in each of the two calls below)
+  auto tile_step = [&](int it, const int cur) {
     // this wave's copies of tile it have landed; after the barrier every
     // wave's have, and every wave is done with tile it-1, whose buffer the
     // copies of tile it+1 overwrite
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    issue(kw.words(), vw.words(), cur ^ 1);
+    issue(kw, vw, cur ^ 1);
     kw.next();
     vw.next();
 
@@ -781,16 +816,24 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     const int kend = sg.end[sc];
     const bool diag = sg.diag[sc];
 
-    // ---- S^T = K Q^T: key blocks 0..15 (s0) and 16..31 (s1) of the tile
-    const __bf16 *Kc = Ks[cur];
+    // ---- S^T = K Q^T: key blocks 0..15 (s0) and 16..31 (s1) of the tile; the
+    // K fragments of the next k-step are read before this one's products
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    auto kread = [&](int ks, int blk) {
+      return *reinterpret_cast<const bf16x8_t *>(kp[ks & 3] + cur * TSZ + 128 * (ks >> 2) + blk * 16 * D);
+    };
+    bf16x8_t ka = kread(0, 0), kb = kread(0, 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const __bf16 *kp = Kc + kbase[ks & 3] + 128 * (ks >> 2);
-      const bf16x8_t k0f = *reinterpret_cast<const bf16x8_t *>(kp);
-      const bf16x8_t k1f = *reinterpret_cast<const bf16x8_t *>(kp + 16 * D);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0f, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1f, qf[ks], s1, 0, 0, 0);
+      bf16x8_t na = ka, nb = kb;
+      if (ks + 1 < KS) {
+        na = kread(ks + 1, 0);
+        nb = kread(ks + 1, 1);
+      }
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[ks], s1, 0, 0, 0);
+      ka = na;
+      kb = nb;
     }
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
 #pragma unroll
@@ -827,12 +870,19 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
 
     // ---- O^T += V^T P^T: lane (d column col of block db, group grp) takes
     // V[4 grp + 0..3][16 db + col] and V[16 + 4 grp + 0..3][16 db + col], two
-    // transposed reads
-    const __bf16 *Vc = Vt[cur];
+    // transposed reads; the next block's are issued before this block's product
+    auto vread = [&](int db) { return v16_read<D>(vp[db & 7] + cur * TSZ + 128 * (db >> 3)); };
+    bf16x8_t vf = vread(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v16_read<D>(Vc + vbase[db & 7] + 128 * (db >> 3)), pf,
-                                                         oacc[db], 0, 0, 0);
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8_t nv = db + 1 < DB ? vread(db + 1) : vf;
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
+      vf = nv;
+    }
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile_step(it, 0);
+    if (it + 1 < ntiles) tile_step(it + 1, 1);
   }
   // the copies issued past the last tile (empty ranges: zeros, no memory read)
   // land before the workgroup's LDS is released
@@ -844,6 +894,11 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   l_sum += __shfl_xor(l_sum, 32);
   const float l_tot = row_ok ? l_sum : 0.f;   // a pad row is stored as a row that saw no key
   if (!row_in) return;
+  // (the row's pointers are formed here, not kept through the loop)
+  const int64_t ri = (qrow0 + (tile * BM + (wave / HG) * RW) + (threadIdx.x & 15)) * a.n_hq + h;
+  float *mptr = a.m + ri;
+  float *dptr = a.den + ri;
+  float *nptr = a.num + ri * (int64_t)D;
   const float m_nat = (m_ref == kNegInf || !row_ok) ? kNegInf : m_ref * a.scale;
   float w_old = 0.f, w_new = 1.f;
   if (a.accumulate) {

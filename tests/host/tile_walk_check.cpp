@@ -33,18 +33,18 @@ static void walk_cmp(const Segs<BN> &sg, int ntiles, const char *blk, uint32_t r
   }
 }
 
-// The per-row copy resources of the head_dim 512 kernel (row_words of the
-// walked tile resource), for every tile t0 .. past the end and every key row q
-// of a 32-key tile and every head offset: a row with keys in range reads the
-// 1 KB of one head inside a visible key row of the tile's segment (every lane
-// offset is below 1 KB); every visible key row of the tile is copied; rows past
-// the visible keys, and every row of a tile past the end, have an empty range.
+// The per-row copy resources of the head_dim 512 kernel (RowWalk), for every
+// tile from 0 to past the end and every key row q of a 32-key tile and every
+// head offset: a row with keys in range reads the 1 KB of one head inside a
+// visible key row of the tile's segment (every lane offset is below 1 KB);
+// every visible key row of the tile is copied; rows past the visible keys, and
+// every row of a tile past the end, have an empty range based at the block
+// start.
 static long long rows_checked = 0;
 static void rows_cmp(const Segs<32> &sg, int ntiles, const char *blk, uint32_t rb, int n_kv) {
-  TileWalk<32> w(sg, ntiles, blk, 1, rb);
+  RowWalk<32> w(sg, ntiles, blk, 0, rb);
   const uint64_t b0 = (uint64_t)(uintptr_t)blk;
-  for (int t = 1; t <= ntiles + 2; ++t, w.next()) {
-    const u32x4_t tw = w.words();
+  for (int t = 0; t <= ntiles + 2; ++t, w.next()) {
     int vis = 0;
     int64_t first = 0;
     if (t < ntiles) {
@@ -55,13 +55,13 @@ static void rows_cmp(const Segs<32> &sg, int ntiles, const char *blk, uint32_t r
     for (int q = 0; q < 32; ++q)
       for (int g = 0; g < n_kv; g += (n_kv > 4 ? n_kv / 4 : 1)) {
         const uint32_t gbase = (uint32_t)g * 1024u;
-        const u32x4_t r = row_words(tw, q, rb, gbase);
+        const u32x4_t r = w.row(q, rb, gbase);
         ++rows_checked;
         const uint64_t base = (uint64_t)(r[1] & 0xFFFFu) << 32 | r[0];
         const bool want = q < vis;
         const bool ok = want ? (r[2] == 1024u && base == b0 + (uint64_t)(first + q) * rb + gbase &&
                                 gbase + 1024u <= rb)
-                             : r[2] == 0u;
+                             : (r[2] == 0u && base == b0);
         if (!ok && ++bad < 10)
           printf("ROW MISMATCH t=%d q=%d g=%d vis=%d nrec=%u base=%llx\n", t, q, g, vis, r[2],
                  (unsigned long long)base);
