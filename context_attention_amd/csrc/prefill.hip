@@ -807,9 +807,6 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
     // copies of tile it+1 overwrite
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    issue(kw, vw, cur ^ 1);
-    kw.next();
-    vw.next();
 
     const int sc = sg.seg(it);
     const int k0 = sg.k0(it);
@@ -823,6 +820,9 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       return *reinterpret_cast<const bf16x8_t *>(kp[ks & 3] + cur * TSZ + 128 * (ks >> 2) + blk * 16 * D);
     };
     bf16x8_t ka = kread(0, 0), kb = kread(0, 1);
+    // the copies of tile it+1 are spread over the k-steps (one per two): issued
+    // together, the 64 copies of the workgroup queue on the CU's load path and
+    // hold up the waves that issue them
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8_t na = ka, nb = kb;
@@ -832,9 +832,19 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       }
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[ks], s1, 0, 0, 0);
+      if ((ks & 1) == 0) {
+        const int i = ks >> 1;   // copy i: K rows for i < CPW, then V rows
+        const int q = wv + NW * (i % CPW);
+        if (i < CPW)
+          dma_1k((i & 1) ? koff1 : koff0, uniform_words(kw.row(q, row_bytes, gbase)), Ks[cur ^ 1] + q * 512);
+        else
+          dma_1k(voff, uniform_words(vw.row(q, row_bytes, gbase)), Vt[cur ^ 1] + q * 512);
+      }
       ka = na;
       kb = nb;
     }
+    kw.next();
+    vw.next();
     if ((k0 + BN > kend) || (diag && k0 + BN - 1 > wrow0)) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
