@@ -17,6 +17,11 @@ Generator definition (identical on every backend):
            x  = fp32(u - 131070) * fp32(UNIT)                      (one fp32 multiply, RNE)
            value = x * scale  (scale a power of two, exact), then RNE to bf16 for bf16 tensors.
 
+mix is the "lowbias32" integer hash published in C. Wellons' hash-prospector
+(xorshift 16, multiply, xorshift 15, multiply, xorshift 15; first multiplier
+0x21F0AAAD), with the top bit of its second multiplier cleared (0x735A2D97 in
+place of 0xD35A2D97) so that the products below fit signed 64-bit integers.
+
 u is a sum of four independent 16-bit uniforms (Irwin-Hall with n = 4), so x has
 mean 0 and variance 1 and a near-normal shape with tails cut at about 3.46. Every
 step is integer arithmetic or one correctly rounded fp32 multiply, so numpy on the
