@@ -313,7 +313,7 @@ struct MfmaArgs {
   int32_t n_kv;
   int32_t nsplit;
   int32_t rep;        // query heads per kv head
-  int32_t ncb;        // 32-head column blocks per kv head
+  int32_t ncb;        // head blocks per kv head (32 heads: decode_mfma; 16 NW: decode_mfma16; 128: decode_wide)
   int32_t xcd_major;  // 1: the ncb workgroups of one key range sit 8 apart (one XCD)
   int64_t shard_len;
   int64_t split_len;
@@ -800,6 +800,252 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma16(MfmaArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// head_dim 512 with more than 112 query heads per kv head (MLA-like layouts)
+// ----------------------------------------------------------------------------
+// The ring step's head_dim 512 loop over a key split: a workgroup of 8 waves
+// (two per SIMD) owns one (shard, batch entry, key split, kv head) and a block
+// of 128 of the kv head's query heads; wave w takes 16 of them as the columns
+// of v_mfma_f32_16x16x32_bf16 in S^T = K Q^T and O^T = V^T P^T over the whole
+// head_dim (64 registers of Q, 128 of accumulator). The 32-key K and V tiles
+// (32 KB each) are copied once per workgroup into double-buffered LDS, each
+// 1 KB key row through a copy resource of its own (RowWalk over the split as a
+// single key segment), and the copies of tile t+1 are spread over the QK^T
+// k-steps of tile t. Heads past the kv group are zero columns, not stored.
+constexpr int kWideWaves = 8;
+constexpr int kWideHeads = 16 * kWideWaves;   // query heads of one workgroup
+
+// What workgroup b of decode_wide owns: shard s, batch entry bi, key split sp
+// ([k_begin, k_end) of the shard's keys), kv head g and head block hs.
+struct WideBlock {
+  int s, bi, sp, g, hs;
+  int64_t k_begin, k_end;
+};
+
+__host__ __device__ __forceinline__ WideBlock wide_block(const MfmaArgs &a, int64_t b) {
+  WideBlock w;
+  int64_t unit;
+  if (a.xcd_major) {
+    const int64_t j = b >> 3;
+    unit = (j / a.ncb) * 8 + (b & 7);
+    w.hs = (int)(j % a.ncb);
+  } else {
+    unit = b / a.ncb;
+    w.hs = (int)(b % a.ncb);
+  }
+  w.g = (int)(unit % a.n_kv);
+  unit /= a.n_kv;
+  w.sp = (int)(unit % a.nsplit);
+  unit /= a.nsplit;
+  w.bi = (int)(unit % a.batch);
+  w.s = (int)(unit / a.batch);
+  w.k_begin = (int64_t)w.sp * a.split_len;
+  w.k_end = a.shard_len < w.k_begin + a.split_len ? a.shard_len : w.k_begin + a.split_len;
+  return w;
+}
+
+// The key split as one key segment of the shard's rows of batch entry bi (the
+// shard holds batch entries one after the other, shard_len rows each).
+template <int BN>
+__host__ __device__ __forceinline__ Segs<BN> split_segs(int bi, int64_t shard_len, int64_t k_begin, int nkeys) {
+  Segs<BN> sg;
+  sg.nseg = nkeys > 0 ? 1 : 0;
+  sg.n0 = (nkeys + BN - 1) / BN;
+  sg.row[0] = (int64_t)bi * shard_len + k_begin;
+  sg.row[1] = 0;
+  sg.end[0] = nkeys;
+  sg.end[1] = 0;
+  sg.diag[0] = false;
+  sg.diag[1] = false;
+  return sg;
+}
+
+__global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_wide(MfmaArgs a) {
+  constexpr int D = 512;
+  constexpr int BN = 32;                        // keys per tile
+  constexpr int NW = kWideWaves;
+  constexpr int KS = D / 32;                    // QK^T k-steps
+  constexpr int DB = D / 16;                    // 16-column blocks of O^T
+  constexpr int TSZ = BN * D;                   // bf16 elements of a K (or V) tile
+  constexpr int CPW = BN / NW;                  // key rows each wave copies per tile
+  static_assert(NW == 8 && CPW % 2 == 0, "the copy offsets assume 8 waves");
+
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][TSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2][TSZ];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 15;     // head of this lane within the wave's 16
+  const int grp = lane >> 4;     // 16-lane group
+
+  const WideBlock wb = wide_block(a, blockIdx.x);
+  const int s = wb.s, bi = wb.bi, sp = wb.sp, g = wb.g;
+  const int nkeys = wb.k_end > wb.k_begin ? (int)(wb.k_end - wb.k_begin) : 0;
+  const int ntiles = (nkeys + BN - 1) / BN;
+
+  const int hc = wb.hs * kWideHeads + wave * 16 + col;   // head of this lane within the kv group
+  const bool head_ok = hc < a.rep;
+  const int h = g * a.rep + (head_ok ? hc : 0);
+  const Segs<BN> sg = split_segs<BN>(bi, a.shard_len, wb.k_begin, nkeys);
+
+  const char *kblock = reinterpret_cast<const char *>(a.k[s]);
+  const char *vblock = reinterpret_cast<const char *>(a.v[s]);
+  const uint32_t row_bytes = (uint32_t)(a.n_kv * D * 2);
+  // copy offsets: key row q = w + 8 i of a tile, swizzled chunk L ^ swizzle(q)
+  // (the ring step's head_dim 512 copies)
+  const int wv = wave;
+  const uint32_t koff0 = (uint32_t)((lane ^ k_swizzle<D>(wv)) * 16);
+  const uint32_t koff1 = (uint32_t)((lane ^ k_swizzle<D>(wv + 8)) * 16);
+  const uint32_t voff = (uint32_t)((lane ^ v16_swizzle<D>(wv)) * 16);
+  const uint32_t gbase = (uint32_t)(g * D * 2);
+  // LDS read addresses: base registers plus immediates (the ring step's layout)
+  const __bf16 *kp[4];
+  const __bf16 *vp[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kp[j] = &Ks[0][col * D + 8 * (4 * (j ^ (col >> 2)) + (grp ^ (col & 3)))];
+  {
+    const int vrow = 4 * grp + (col >> 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vp[j] = &Vt[0][vrow * D + 16 * (j ^ (vrow & 7)) + 8 * ((col >> 1) & 1) + 4 * (col & 1)];
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  const float thr = kRescaleLog2 / sl2;
+  float m_ref = kNegInf, l_run = 0.f;
+  f32x4_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    RowWalk<BN> kw(sg, ntiles, kblock, 0, row_bytes), vw(sg, ntiles, vblock, 0, row_bytes);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int q = wv + NW * i;
+      dma_1k((i & 1) ? koff1 : koff0, uniform_words(kw.row(q, row_bytes, gbase)), Ks[0] + q * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int q = wv + NW * i;
+      dma_1k(voff, uniform_words(vw.row(q, row_bytes, gbase)), Vt[0] + q * 512);
+    }
+    kw.next();
+    vw.next();
+
+    // Q fragments (B operand of S^T = K Q^T): lane holds q[h][32 ks + 8 grp .. +8]
+    bf16x8_t qf[KS];
+    {
+      const __bf16 *qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)bi * a.n_hq + h) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = head_ok ? *reinterpret_cast<const bf16x8_t *>(qp + 32 * ks)
+                         : __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+    }
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    auto tile_step = [&](int it, const int cur) {
+      // this wave's copies of tile it have landed; after the barrier every
+      // wave's have, and every wave is done with tile it-1, whose buffer the
+      // copies of tile it+1 overwrite
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      const int k0 = it * BN;
+
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      auto kread = [&](int ks, int blk) {
+        return *reinterpret_cast<const bf16x8_t *>(kp[ks & 3] + cur * TSZ + 128 * (ks >> 2) + blk * 16 * D);
+      };
+      bf16x8_t ka = kread(0, 0), kb = kread(0, 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t na = ka, nb = kb;
+        if (ks + 1 < KS) {
+          na = kread(ks + 1, 0);
+          nb = kread(ks + 1, 1);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qf[ks], s1, 0, 0, 0);
+        if ((ks & 1) == 0) {
+          const int i = ks >> 1;   // copy i of tile it+1: K rows for i < CPW, then V rows
+          const int q = wv + NW * (i % CPW);
+          if (i < CPW)
+            dma_1k((i & 1) ? koff1 : koff0, uniform_words(kw.row(q, row_bytes, gbase)), Ks[cur ^ 1] + q * 512);
+          else
+            dma_1k(voff, uniform_words(vw.row(q, row_bytes, gbase)), Vt[cur ^ 1] + q * 512);
+        }
+        ka = na;
+        kb = nb;
+      }
+      kw.next();
+      vw.next();
+      if (k0 + BN > nkeys) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (k0 + 4 * grp + t >= nkeys) s0[t] = kNegInf;
+          if (k0 + 16 + 4 * grp + t >= nkeys) s1[t] = kNegInf;
+        }
+      }
+
+      // online softmax: the head's 32 keys lie in the 4 lanes col, col + 16, ...
+      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      mx = max_across_rows16(mx);
+      mx = max_across_halves(mx);
+      if (__any(mx > m_ref + thr)) {
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast((m_ref - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        m_ref = m_new;
+      }
+      const float mref = (m_ref == kNegInf) ? 0.f : m_ref * sl2;
+      uint32_t pk[4];
+      pk[0] = pack_bf16x2(exp2_fast(fmaf(s0[0], sl2, -mref)), exp2_fast(fmaf(s0[1], sl2, -mref)));
+      pk[1] = pack_bf16x2(exp2_fast(fmaf(s0[2], sl2, -mref)), exp2_fast(fmaf(s0[3], sl2, -mref)));
+      pk[2] = pack_bf16x2(exp2_fast(fmaf(s1[0], sl2, -mref)), exp2_fast(fmaf(s1[1], sl2, -mref)));
+      pk[3] = pack_bf16x2(exp2_fast(fmaf(s1[2], sl2, -mref)), exp2_fast(fmaf(s1[3], sl2, -mref)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[i]), ones, l_run, false);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+
+      // O^T += V^T P^T, the next block's transposed reads ahead of this block's product
+      auto vread = [&](int db) { return v16_read<D>(vp[db & 7] + cur * TSZ + 128 * (db >> 3)); };
+      bf16x8_t vf = vread(0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8_t nv = db + 1 < DB ? vread(db + 1) : vf;
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[db], 0, 0, 0);
+        vf = nv;
+      }
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+      tile_step(it, 0);
+      if (it + 1 < ntiles) tile_step(it + 1, 1);
+    }
+    // the copies issued past the last tile (empty ranges: zeros, no memory
+    // read) land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+
+  // ---- epilogue: the split's triple of each head (natural-log max); the 4
+  // groups hold disjoint keys, so their denominators add up
+  float l_sum = l_run + __shfl_xor(l_run, 16);
+  l_sum += __shfl_xor(l_sum, 32);
+  if (head_ok) {
+    const int64_t wi = ((((int64_t)s * a.batch + bi) * a.n_hq + (int64_t)g * a.rep) + hc) * a.nsplit + sp;
+    if (grp == 0) {
+      a.ws_m[wi] = (m_ref == kNegInf) ? kNegInf : m_ref * a.scale;
+      a.ws_den[wi] = l_sum;
+    }
+    float *np = a.ws_num + wi * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4_t *>(np + 16 * db) = oacc[db];
+  }
+}
+
 // Wave-wide max and sum (butterfly over the 64 lanes).
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -934,7 +1180,8 @@ void plan_splits(int64_t shard_len, int64_t step, int64_t groups, int64_t target
 // The partial kernel a description runs on and its split geometry.
 struct DecodePlan {
   bool mfma;       // decode_mfma (else decode_partial)
-  bool mfma16;     // decode_mfma16 (takes precedence)
+  bool mfma16;     // decode_mfma16 (takes precedence over decode_mfma)
+  bool wide;       // decode_wide (takes precedence over both)
   int G;           // query heads per kv head
   int gv;          // decode_partial: query heads per block
   int ncb;         // decode_mfma: 32-head column blocks per kv head; decode_mfma16: head blocks of 16 NW
@@ -954,6 +1201,9 @@ DecodePlan plan_decode(const cpattn_decode_desc &d) {
   // more than 32 heads per kv head: one workgroup serves up to 128 of them from
   // one copy of each K and V tile
   p.mfma16 = d.dtype == CPATTN_DT_BF16 && p.G > 32;
+  // head_dim 512 with at least 8 blocks of 16 heads: 8 waves of the ring step's
+  // head_dim 512 loop, 128 heads per workgroup
+  p.wide = p.mfma16 && d.head_dim == 512 && (p.G + 15) / 16 >= kWideWaves;
   p.gv = p.G <= 8 ? p.G : 8;
   p.ncb = (p.G + 31) / 32;
   p.nw = 0;
@@ -961,7 +1211,12 @@ DecodePlan plan_decode(const cpattn_decode_desc &d) {
   // about 512 workgroups for the two matrix-core kernels: measured on MI355X,
   // 2-4% faster than 2048 on the single-kv-head layouts (a workgroup's prologue
   // and final merge are paid once per split) and level on GQA 32/4
-  if (p.mfma16) {
+  if (p.wide) {
+    p.nw = kWideWaves;
+    p.ncb = (p.G + kWideHeads - 1) / kWideHeads;
+    const int64_t groups = (int64_t)d.cp * d.batch * d.n_kv * p.ncb;
+    plan_splits(shard_len, 32, groups, 512, p.nsplit, p.split_len);
+  } else if (p.mfma16) {
     const int blk16 = (p.G + 15) / 16;
     // head_dim 512 keeps 4 waves (one per SIMD): 8 would not fit their Q and
     // accumulators in the registers of two waves per SIMD
@@ -1027,6 +1282,32 @@ hipError_t launch_mfma(const MfmaArgs &a, int D, int64_t blocks, hipStream_t s) 
   return hipGetLastError();
 }
 
+// Arguments of the matrix-core partial kernels for a description and its plan.
+MfmaArgs mfma_args(const cpattn_decode_desc &d, const DecodePlan &p, const void *q, const void *const *k_shards,
+                   const void *const *v_shards, float *ws_m, float *ws_den, float *ws_num) {
+  MfmaArgs a;
+  a.q = q;
+  for (int s = 0; s < d.cp; ++s) {
+    a.k[s] = k_shards[s];
+    a.v[s] = v_shards[s];
+  }
+  a.ws_m = ws_m;
+  a.ws_den = ws_den;
+  a.ws_num = ws_num;
+  a.batch = d.batch;
+  a.n_hq = d.n_hq;
+  a.n_kv = d.n_kv;
+  a.nsplit = p.nsplit;
+  a.rep = d.n_hq / d.n_kv;
+  a.ncb = p.ncb;
+  const int64_t units = (int64_t)d.cp * d.batch * p.nsplit;
+  a.xcd_major = (p.ncb > 1 && (units * d.n_kv) % 8 == 0) ? 1 : 0;
+  a.shard_len = d.kv_len / d.cp;
+  a.split_len = p.split_len;
+  a.scale = d.scale;
+  return a;
+}
+
 // The pass-Q decode of cpattn_passq_decode with the workspace given (ws ==
 // nullptr: only the size is stored).
 int passq_decode(const cpattn_decode_desc *desc, const void *q, const void *const *k_shards,
@@ -1072,26 +1353,13 @@ int passq_decode(const cpattn_decode_desc *desc, const void *q, const void *cons
   float *ws_m = wsf, *ws_den = wsf + triples, *ws_num = wsf + 2 * triples;
   hipError_t e;
   if (p.mfma || p.mfma16) {
-    MfmaArgs a;
-    a.q = q;
-    for (int s = 0; s < d.cp; ++s) {
-      a.k[s] = k_shards[s];
-      a.v[s] = v_shards[s];
+    const MfmaArgs a = mfma_args(d, p, q, k_shards, v_shards, ws_m, ws_den, ws_num);
+    if (p.wide) {
+      hipLaunchKernelGGL(decode_wide, dim3((unsigned)blocks), dim3(64 * kWideWaves), 0, stream, a);
+      e = hipGetLastError();
+    } else {
+      e = p.mfma16 ? launch_mfma16(a, d.head_dim, p.nw, blocks, stream) : launch_mfma(a, d.head_dim, blocks, stream);
     }
-    a.ws_m = ws_m;
-    a.ws_den = ws_den;
-    a.ws_num = ws_num;
-    a.batch = d.batch;
-    a.n_hq = d.n_hq;
-    a.n_kv = d.n_kv;
-    a.nsplit = nsplit;
-    a.rep = G;
-    a.ncb = p.ncb;
-    a.xcd_major = (p.ncb > 1 && (units * d.n_kv) % 8 == 0) ? 1 : 0;
-    a.shard_len = d.kv_len / d.cp;
-    a.split_len = p.split_len;
-    a.scale = d.scale;
-    e = p.mfma16 ? launch_mfma16(a, d.head_dim, p.nw, blocks, stream) : launch_mfma(a, d.head_dim, blocks, stream);
   } else {
     DecodeArgs a;
     a.q = q;

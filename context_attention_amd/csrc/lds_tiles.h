@@ -180,4 +180,59 @@ __device__ __forceinline__ f32x16_t get_scores(const f32x4_t (*x)[64]) {
   return s;
 }
 
+// Tile geometry of flattened tile index t over the (up to two) key segments.
+template <int BN>
+struct Segs {
+  int nseg;               // non-empty segments (0, 1 or 2)
+  int n0;                 // tiles of segment 0
+  int64_t row[2];         // first key row of each segment in the block
+  int end[2];             // visible keys of each segment
+  bool diag[2];
+  __host__ __device__ __forceinline__ int seg(int t) const { return t < n0 ? 0 : 1; }
+  __host__ __device__ __forceinline__ int k0(int t) const { return (t < n0 ? t : t - n0) * BN; }
+  __host__ __device__ __forceinline__ int tiles() const {
+    return n0 + (nseg > 1 ? (end[1] + BN - 1) / BN : 0);
+  }
+};
+
+// The copy resources of the head_dim 512 kernels (ring step and decode), one per key row of a tile,
+// walked tile by tile in scalar registers: for tile t (t0, t0 + 1, ...) and key
+// row q, the 1 KB of one head at byte gbase of the row, based there with 1 KB
+// in range when the row holds a visible key, and otherwise (rows past the
+// segment's visible keys, tiles past the last) an empty range at the block
+// start (the copy then writes zeros and touches no memory).
+template <int BN>
+struct RowWalk {
+  int t, n0, ntiles;
+  uint64_t blk;
+  uint64_t addr, addr1;    // first key row of tile t; of the second segment's first tile
+  int left, left1;         // visible keys from there to the segment's end
+  uint32_t step;           // bytes of one tile
+  __host__ __device__ __forceinline__ RowWalk(const Segs<BN> &sg, int ntiles_, const char *blk_, int t0, uint32_t rb)
+      : t(t0), n0(sg.n0), ntiles(ntiles_), blk((uint64_t)(uintptr_t)blk_) {
+    const int s = sg.seg(t0), k = sg.k0(t0);
+    addr = blk + (uint64_t)((sg.row[s] + k) * (int64_t)rb);
+    left = sg.end[s] - k;
+    addr1 = blk + (uint64_t)(sg.row[1] * (int64_t)rb);
+    left1 = sg.end[1];
+    step = (uint32_t)BN * rb;
+  }
+  __host__ __device__ __forceinline__ void next() {
+    ++t;
+    if (t == n0) {
+      addr = addr1;
+      left = left1;
+    } else {
+      addr += step;
+      left -= BN;
+    }
+  }
+  // q * rb + gbase fits 32 bits: both callers reject key rows of 2^25 bytes or more
+  __host__ __device__ __forceinline__ u32x4_t row(int q, uint32_t rb, uint32_t gbase) const {
+    const bool ok = t < ntiles && q < left;
+    const uint64_t base = ok ? addr + (uint32_t)((uint32_t)q * rb + gbase) : blk;
+    return u32x4_t{(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, ok ? 1024u : 0u, kBufferWord3};
+  }
+};
+
 }  // namespace cpattn

@@ -32,6 +32,11 @@ CASES = [
     ("gqa128-bf16-d128-8-waves", 2, 4 * 100, 4, 256, 2, 128, "bf16"),
     ("mqa96-bf16-d64-partial-head-blocks", 2, 2 * 777, 2, 96, 1, 64, "bf16"),
     ("mqa64-bf16-one-key-shards", 1, 8, 8, 64, 1, 128, "bf16"),
+    # head_dim 512 with more than 112 query heads per kv head (decode_wide: 128 heads per workgroup)
+    ("mla-like-128-bf16-d512-ragged-shards", 3, 3 * 1001, 3, 128, 1, 512, "bf16"),
+    ("gqa128-bf16-d512-two-kv-heads", 2, 2 * 500, 2, 256, 2, 512, "bf16"),
+    ("mqa192-bf16-d512-partial-head-block", 1, 4 * 200, 4, 192, 1, 512, "bf16"),
+    ("mqa136-bf16-d512-one-key-shards", 2, 8, 8, 136, 1, 512, "bf16"),
     ("mqa16-f32-d128-head-blocks", 2, 2 * 500, 2, 16, 1, 128, "f32"),
     ("gqa16-f32-d64-two-kv-heads", 2, 2 * 300, 2, 32, 2, 64, "f32"),
 ]
