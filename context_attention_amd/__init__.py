@@ -38,7 +38,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20    # CPATTN_NOALLOC_SCRATCH_BYTES
 EXPORTS = ["cpattn_balanced_split", "cpattn_balanced_split_padded", "cpattn_local_rows", "cpattn_ring_step_partial",
            "cpattn_ring_pass",
            "cpattn_ring_prefill_overlapped", "cpattn_merge", "cpattn_tree_reduce", "cpattn_passq_decode",
-           "cpattn_passq_decode_noalloc",
+           "cpattn_passq_decode_noalloc", "cpattn_ulysses_all_to_all",
            "cpattn_account", "cpattn_version"]
 
 
@@ -116,6 +116,7 @@ def load():
     lib.cpattn_passq_decode.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp,
                                         ctypes.POINTER(ctypes.c_size_t), vp]
+    lib.cpattn_ulysses_all_to_all.argtypes = [i32, i64, i32, i64, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]
     lib.cpattn_passq_decode_noalloc.argtypes = [ctypes.POINTER(_DecodeDesc), vp, ctypes.POINTER(vp),
                                                 ctypes.POINTER(vp), ctypes.POINTER(_Partial), vp, vp, vp]
     lib.cpattn_account.argtypes = [ctypes.POINTER(_AccountIn), ctypes.POINTER(_AccountOut)]
@@ -329,6 +330,43 @@ def ring_pass(src, dst, workgroups: int, stream=None) -> None:
         raise ValueError("src and dst sizes differ")
     _check(lib.cpattn_ring_pass(src.data_ptr(), dst.data_ptr(), nbytes, workgroups, _stream(stream)),
            "cpattn_ring_pass")
+
+
+def ulysses_all_to_all(src, dst, n_heads: int, direction: str, stream=None) -> None:
+    """cpattn_ulysses_all_to_all over n = len(src) ranks. direction "seq_to_head":
+    src[j] [rows, n_heads, *head] -> dst[i] [n*rows, n_heads/n, *head];
+    "head_to_seq": the inverse (src[i] [n*rows, n_heads/n, *head] ->
+    dst[j] [rows, n_heads, *head]). Every tensor contiguous, on the device, of
+    one dtype."""
+    lib = load()
+    n = len(src)
+    if n < 1 or len(dst) != n:
+        raise ValueError("src and dst must hold the same number (>= 1) of ranks")
+    if direction not in ("seq_to_head", "head_to_seq"):
+        raise ValueError("direction must be 'seq_to_head' or 'head_to_seq'")
+    if n_heads % n:
+        raise ValueError(f"n_heads {n_heads} is not a multiple of the {n} ranks")
+    seq, head = (src, dst) if direction == "seq_to_head" else (dst, src)
+    rows = seq[0].shape[0]
+    inner = tuple(seq[0].shape[2:])
+    want_seq, want_head = (rows, n_heads) + inner, (n * rows, n_heads // n) + inner
+    for t in seq:
+        if tuple(t.shape) != want_seq:
+            raise ValueError(f"sequence-sharded shape {tuple(t.shape)}, expected {want_seq}")
+    for t in head:
+        if tuple(t.shape) != want_head:
+            raise ValueError(f"head-sharded shape {tuple(t.shape)}, expected {want_head}")
+    for t in list(src) + list(dst):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != seq[0].dtype:
+            raise ValueError("contiguous device tensors of one dtype expected")
+    head_bytes = seq[0].element_size()
+    for x in inner:
+        head_bytes *= x
+    ps = (ctypes.c_void_p * n)(*[t.data_ptr() for t in src])
+    pd = (ctypes.c_void_p * n)(*[t.data_ptr() for t in dst])
+    _check(lib.cpattn_ulysses_all_to_all(n, rows, n_heads, head_bytes, ps, pd,
+                                         0 if direction == "seq_to_head" else 1, _stream(stream)),
+           "cpattn_ulysses_all_to_all")
 
 
 class RingEvents:

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcpattn.so")
 
-HIP_SOURCES = ["prefill.hip", "merge.hip", "decode.hip", "ring.hip"]
+HIP_SOURCES = ["prefill.hip", "merge.hip", "decode.hip", "ring.hip", "ulysses.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -10,8 +10,8 @@
  * Around them: the one-GPU emulation of the ring's block transfers overlapped
  * with its compute (the spec's dependency contract), a padded layout for
  * sequence lengths not divisible by 2*cp (after the padding rule of the TP/EP
- * design page), and a tree-order reduction of triples (the spec's follow-up
- * work). Sections cited below are sections of the G5 spec unless another page
+ * design page), a tree-order reduction of triples and the all-to-all of
+ * Ulysses and hybrid CP (the spec's follow-up work). Sections cited below are sections of the G5 spec unless another page
  * is named.
  *
  * Conventions shared by every entry point
@@ -268,6 +268,32 @@ int cpattn_merge(int64_t rows, int32_t n_hq, int32_t head_dim,
  * Errors: E_ARG (bad counts, null or repeated parts), E_UNSUPPORTED, E_DEVICE. */
 int cpattn_tree_reduce(int64_t rows, int32_t n_hq, int32_t head_dim, const cpattn_partial *parts,
                        int32_t n_parts, float *out, float *lse, hipStream_t stream);
+
+/* All-to-all of a Ulysses group of n ranks, every rank emulated on this GPU:
+ * the exchange of Ulysses sequence parallelism, which the spec names as the
+ * follow-up to its pass-KV ring together with hybrid CP (Limitations and
+ * follow-up work) and leaves out of its own scope (Goals and non-goals). A
+ * sequence is held sharded by tokens (rank j: `rows` token rows x n_heads
+ * heads) or sharded by heads (rank i: all n*rows token rows x the hn =
+ * n_heads/n heads [i*hn, (i+1)*hn), the rows of rank j at rows j*rows ..
+ * (j+1)*rows-1 in their own order); a head is head_bytes bytes (head_dim
+ * elements of Q, K, V or an output, or one log-sum-exp):
+ *   direction 0, seq -> head:  dst[i][j*rows + r][h] = src[j][r][i*hn + h]
+ *   direction 1, head -> seq:  dst[j][r][i*hn + h]   = src[i][j*rows + r][h]
+ *   src, dst  HOST arrays of n device pointers, each buffer rows*n_heads*
+ *             head_bytes bytes (the same in both layouts), 4-byte aligned
+ *             (16-byte alignment and 16-byte multiples of hn*head_bytes take
+ *             the faster path). No destination overlaps a source or another
+ *             destination.
+ *   head_bytes > 0, a multiple of 4; 1 <= n <= 64.
+ * Byte-exact: a permutation of the source bytes. The attention of a Ulysses
+ * rank over its heads is then a ring step over the whole sequence (cp = 1), and
+ * of a hybrid group (u Ulysses ranks inside each of c ring ranks) the pass-KV
+ * ring over c ranks on its heads.
+ * Errors: E_ARG, E_DIVISIBILITY (n_heads % n), E_UNSUPPORTED (n > 64, sizes past
+ * int64), E_DEVICE. */
+int cpattn_ulysses_all_to_all(int32_t n, int64_t rows, int32_t n_heads, int64_t head_bytes,
+                              const void *const *src, void *const *dst, int32_t direction, hipStream_t stream);
 
 /* Pass-Q decode (Definitions table, "Pass-Q"; Use case, decode): the query is
  * sent to every shard, shard s computes the partial triple over its kv_len/cp

@@ -100,3 +100,22 @@ def test_ring_prefill_overlapped_checks_shapes_and_counts():
         with pytest.raises(ValueError, match="acc shape"):
             ca.ring_prefill_overlapped(desc, qs, ks, ks, rx, rx, [acc[0], bad], 4)
     _device_error(lambda: ca.ring_prefill_overlapped(desc, qs, ks, ks, rx, rx, acc, 4))
+
+
+def test_ulysses_all_to_all_checks_shapes_and_direction():
+    n, rows, heads, d = 2, 4, 4, 64
+    src = [torch.zeros(rows, heads, d, dtype=torch.bfloat16) for _ in range(n)]
+    dst = [torch.zeros(n * rows, heads // n, d, dtype=torch.bfloat16) for _ in range(n)]
+    with pytest.raises(ValueError, match="direction"):
+        ca.ulysses_all_to_all(src, dst, heads, "sideways")
+    with pytest.raises(ValueError, match="multiple"):
+        ca.ulysses_all_to_all(src, dst, 3, "seq_to_head")
+    with pytest.raises(ValueError, match="same number"):
+        ca.ulysses_all_to_all(src, dst[:1], heads, "seq_to_head")
+    with pytest.raises(ValueError, match="head-sharded shape"):
+        ca.ulysses_all_to_all(src, [torch.zeros(rows, heads, d, dtype=torch.bfloat16)] * n, heads, "seq_to_head")
+    with pytest.raises(ValueError, match="sequence-sharded shape"):
+        ca.ulysses_all_to_all(dst, [torch.zeros(rows + 1, heads, d, dtype=torch.bfloat16), src[1]], heads,
+                              "head_to_seq")
+    with pytest.raises(ValueError, match="device tensors"):
+        ca.ulysses_all_to_all(src, dst, heads, "seq_to_head")

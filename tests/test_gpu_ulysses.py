@@ -1,0 +1,130 @@
+"""GPU tests of the Ulysses all-to-all (cpattn_ulysses_all_to_all) and of
+Ulysses and hybrid CP built from it and the ring step (G5 context-parallel
+modelling spec, "Limitations and follow-up work": Ulysses and hybrid CP).
+
+The all-to-all is a byte permutation: compared bit for bit with the same
+permutation written with torch indexing, in both directions, with the bytes
+past every destination left alone. Ulysses: the sequence is sharded by tokens
+over u ranks; the all-to-all gives each rank all tokens of n_hq/u query heads
+and n_kv/u kv heads, the rank runs causal attention over the whole sequence
+for its heads (one ring step with cp = 1), and the inverse all-to-all brings
+the outputs back to the token shards. Hybrid: u Ulysses ranks inside each of c
+ring ranks (cp = u c): ring rank j holds the balanced split's rows of j over c
+ranks, its u Ulysses ranks hold consecutive slices of those rows; the
+all-to-all inside each ring group, then the pass-KV ring over the c ring ranks
+on each head group, then the inverse all-to-all. Outputs and log-sum-exps are
+compared with the oracle's unsplit attention at the global positions of each
+rank's rows."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL_BF16, TOL_F32, compare, global_inputs_np, log, need_gpu, np_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch_seq_to_head(src, n):
+    """The seq -> head layout by indexing: dst[i] = rows of every rank, heads of group i."""
+    import torch
+    hn = src[0].shape[1] // n
+    return [torch.cat([s[:, i * hn:(i + 1) * hn] for s in src], dim=0).contiguous() for i in range(n)]
+
+
+@pytest.mark.parametrize("n,rows,heads,inner,dtype", [
+    (1, 7, 4, (64,), "bf16"), (2, 5, 4, (128,), "bf16"), (4, 33, 8, (128,), "bf16"), (8, 16, 32, (128,), "bf16"),
+    (3, 9, 6, (512,), "bf16"), (4, 12, 8, (), "f32"), (2, 3, 6, (3,), "f32"), (4, 0, 8, (128,), "bf16"),
+    (8, 20, 64, (128,), "f32")])
+def test_all_to_all_is_the_permutation(n, rows, heads, inner, dtype):
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    log(f"ulysses all-to-all n={n} rows={rows} heads={heads} head={inner} {dtype}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(n * 1000 + rows)
+    src = [torch.randn((rows, heads) + inner, generator=g, device="cuda").to(tdt) for _ in range(n)]
+    want = _torch_seq_to_head(src, n)
+    # destinations as views at the front of larger buffers, the tails poisoned
+    numel = rows * heads * int(np.prod(inner))
+    big = [torch.full((numel + 64,), 7, dtype=tdt, device="cuda") for _ in range(n)]
+    dst = [b[:numel].view((n * rows, heads // n) + inner) for b in big]
+    ca.ulysses_all_to_all(src, dst, heads, "seq_to_head")
+    back_big = [torch.full((numel + 64,), 5, dtype=tdt, device="cuda") for _ in range(n)]
+    back = [b[:numel].view((rows, heads) + inner) for b in back_big]
+    ca.ulysses_all_to_all(dst, back, heads, "head_to_seq")
+    torch.cuda.synchronize()
+    for i in range(n):
+        assert torch.equal(dst[i].view(torch.int16 if dtype == "bf16" else torch.int32),
+                           want[i].view(torch.int16 if dtype == "bf16" else torch.int32)), f"rank {i} differs"
+        assert torch.all(big[i][numel:] == 7), "write past the end of a destination"
+        assert torch.equal(back[i], src[i]), f"round trip differs on rank {i}"
+        assert torch.all(back_big[i][numel:] == 5), "write past the end of a destination"
+
+
+def _check_rank(name, out_seq, lse_seq, pos, ref_out, ref_lse, tol):
+    compare(name, out_seq.cpu().numpy(), lse_seq.cpu().numpy(), ref_out[pos], ref_lse[pos], tol)
+
+
+CASES = [
+    # lens, u (Ulysses ranks), c (ring ranks), n_hq, n_kv, d, dtype
+    ([1024], 4, 1, 16, 4, 128, "bf16"),
+    ([768, 256], 2, 1, 8, 2, 64, "bf16"),
+    ([1024], 2, 4, 16, 4, 128, "bf16"),
+    ([512, 1024], 4, 2, 16, 8, 128, "bf16"),
+    ([640], 2, 2, 8, 2, 64, "f32"),
+    ([512], 2, 2, 8, 4, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("lens,u,c,n_hq,n_kv,d,dtype", CASES,
+                         ids=[f"u{x[1]}-c{x[2]}-{x[6]}-d{x[5]}-{len(x[0])}seq" for x in CASES])
+def test_ulysses_and_hybrid_match_the_oracle(lens, u, c, n_hq, n_kv, d, dtype):
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    log(f"ulysses/hybrid lens={lens} u={u} c={c} heads={n_hq}/{n_kv} d={d} {dtype}")
+    scale = 1.0 / np.sqrt(d)
+    qn, kn, vn, cu = global_inputs_np(lens, n_hq, n_kv, d, seed=41, dtype=dtype, scale=0.5)
+    q, k, v = (np_to_device(a, dtype) for a in (qn, kn, vn))
+    ref_out, ref_lse = oracle.attention_reference(qn, kn, vn, cu, scale)
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    # ring rank j: the balanced split's rows over c ranks; Ulysses rank i of it: slice i of those rows
+    pos = [ca.balanced_split(cu, c, j)[0] for j in range(c)]
+    L = len(pos[0])
+    assert L % u == 0
+    R = L // u
+    idx = [torch.from_numpy(p).to("cuda") for p in pos]
+    seq = {name: [[t.index_select(0, idx[j][i * R:(i + 1) * R]).contiguous() for i in range(u)] for j in range(c)]
+           for name, t in (("q", q), ("k", k), ("v", v))}
+    # all-to-all inside each ring group: head-sharded [L, heads/u, d] per (i, j)
+    head = {}
+    for name, nh in (("q", n_hq), ("k", n_kv), ("v", n_kv)):
+        head[name] = []
+        for j in range(c):
+            dst = [torch.empty((L, nh // u, d), dtype=seq[name][j][0].dtype, device="cuda") for _ in range(u)]
+            ca.ulysses_all_to_all(seq[name][j], dst, nh, "seq_to_head")
+            head[name].append(dst)
+    # the pass-KV ring over the c ring ranks on each head group
+    desc = ca.PrefillDesc(cp=c, cu_seqlens=cu, n_hq=n_hq // u, n_kv=n_kv // u, head_dim=d, dtype=dtype, scale=scale)
+    out_h = [[None] * u for _ in range(c)]
+    lse_h = [[None] * u for _ in range(c)]
+    for i in range(u):
+        for r in range(c):
+            acc = ca.new_partial(L, n_hq // u, d)
+            for t in range(c):
+                j = (r - t) % c
+                ca.ring_step_partial(desc, r, t, head["q"][r][i], head["k"][j][i], head["v"][j][i], acc,
+                                     accumulate=t > 0)
+            out_h[r][i] = torch.empty(L, n_hq // u, d, device="cuda")
+            lse_h[r][i] = torch.empty(L, n_hq // u, device="cuda")
+            ca.merge(acc, [], out=out_h[r][i], lse=lse_h[r][i])
+    # back to the token shards and against the oracle
+    for r in range(c):
+        out_s = [torch.empty(R, n_hq, d, device="cuda") for _ in range(u)]
+        lse_s = [torch.empty(R, n_hq, device="cuda") for _ in range(u)]
+        ca.ulysses_all_to_all(out_h[r], out_s, n_hq, "head_to_seq")
+        ca.ulysses_all_to_all(lse_h[r], lse_s, n_hq, "head_to_seq")
+        torch.cuda.synchronize()
+        for i in range(u):
+            _check_rank(f"ring rank {r}, Ulysses rank {i}", out_s[i], lse_s[i], pos[r][i * R:(i + 1) * R],
+                        ref_out, ref_lse, tol)

@@ -6,7 +6,8 @@
   * the host programs that include the kernel sources and check their scalar
     helpers (tests/host/tile_walk_check.cpp: copy resources;
     tests/host/decode_plan_check.cpp: decode key splits;
-    tests/host/decode_wide_check.cpp: the head_dim 512 decode's indexing), built with hipcc with
+    tests/host/decode_wide_check.cpp: the head_dim 512 decode's indexing;
+    tests/host/a2a_check.cpp: the Ulysses all-to-all), built with hipcc with
     the sanitizers on the host side only (each -fsanitize= after -Xarch_host;
     no GPU code is involved).
 Any sanitizer report aborts the program (-fno-sanitize-recover=all)."""
@@ -46,7 +47,8 @@ def test_host_api_under_sanitizers(tmp_path):
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 @pytest.mark.parametrize("src,marker", [("decode_plan_check.cpp", " 0 failures"),
                                         ("tile_walk_check.cpp", " 0 mismatches"),
-                                        ("decode_wide_check.cpp", " 0 failures")])
+                                        ("decode_wide_check.cpp", " 0 failures"),
+                                        ("a2a_check.cpp", " 0 failures")])
 def test_kernel_host_helpers_under_sanitizers(tmp_path, src, marker):
     exe = str(tmp_path / src.replace(".cpp", ""))
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
