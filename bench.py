@@ -308,6 +308,64 @@ def _decode_gbs(ca, torch, b, S, cp, H, G, d, reps=5):
             "frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": byts}
 
 
+def _ulysses_gqa(ca, synth, torch, w, u=8, reps=3):
+    """Ulysses attention of a prefill workload over u ranks emulated on the GPU:
+    the token shards (u consecutive row slices) of Q, K, V go through the
+    all-to-all to head shards (n_hq/u query, n_kv/u kv heads over all tokens),
+    each rank runs the unsplit causal attention over its heads (a ring step with
+    cp = 1, then finalize), and out and lse go back through the inverse
+    all-to-all. Reported: the all-to-all's HBM throughput (every byte read once
+    and written once) and the attention's TFLOP/s (exact causal FLOPs over the
+    summed kernel time), each from HIP events; median over reps."""
+    S, H, G, d = w.total_tokens, w.n_hq, w.n_kv, w.head_dim
+    R = S // u
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, "cuda")
+    seq = {n: [t[i * R:(i + 1) * R].contiguous() for i in range(u)] for n, t in (("q", q), ("k", k), ("v", v))}
+    del q, k, v
+    head = {n: [torch.empty(S, nh // u, d, dtype=seq[n][0].dtype, device="cuda") for _ in range(u)]
+            for n, nh in (("q", H), ("k", G), ("v", G))}
+    desc = ca.PrefillDesc(cp=1, cu_seqlens=w.cu_seqlens, n_hq=H // u, n_kv=G // u, head_dim=d, dtype=w.dtype,
+                          scale=w.softmax_scale)
+    acc = [ca.new_partial(S, H // u, d) for _ in range(u)]
+    out_h = [torch.empty(S, H // u, d, device="cuda") for _ in range(u)]
+    lse_h = [torch.empty(S, H // u, device="cuda") for _ in range(u)]
+    out_s = [torch.empty(R, H, d, device="cuda") for _ in range(u)]
+    lse_s = [torch.empty(R, H, device="cuda") for _ in range(u)]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a2a_ms, att_ms, tot_ms = [], [], []
+    for rep_i in range(reps + 1):
+        e = [ev() for _ in range(5)]
+        e[0].record(stream)
+        for n, nh in (("q", H), ("k", G), ("v", G)):
+            ca.ulysses_all_to_all(seq[n], head[n], nh, "seq_to_head")
+        e[1].record(stream)
+        for i in range(u):
+            ca.ring_step_partial(desc, 0, 0, head["q"][i], head["k"][i], head["v"][i], acc[i], accumulate=False)
+        e[2].record(stream)
+        for i in range(u):
+            ca.merge(acc[i], [], out=out_h[i], lse=lse_h[i])
+        e[3].record(stream)
+        ca.ulysses_all_to_all(out_h, out_s, H, "head_to_seq")
+        ca.ulysses_all_to_all(lse_h, lse_s, H, "head_to_seq")
+        e[4].record(stream)
+        torch.cuda.synchronize()
+        if rep_i:
+            a2a_ms.append(e[0].elapsed_time(e[1]) + e[3].elapsed_time(e[4]))
+            att_ms.append(e[1].elapsed_time(e[2]))
+            tot_ms.append(e[0].elapsed_time(e[4]))
+    a2a_bytes = 2 * (S * (H + 2 * G) * d * 2 + S * H * (d + 1) * 4)
+    flops = ca.account(cp=1, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=w.cu_seqlens)["rank_flops_exact"]
+    a, t, tot = float(np.median(a2a_ms)), float(np.median(att_ms)), float(np.median(tot_ms))
+    return {"u": u, "all_to_all_ms": round(a, 3), "all_to_all_gb_per_s": round(a2a_bytes / (a * 1e-3) / 1e9, 1),
+            "all_to_all_frac": round(a2a_bytes / (a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "all_to_all_bytes": a2a_bytes,
+            "attention_ms": round(t, 3), "attention_tflops": round(flops / (t * 1e-3) / 1e12, 1),
+            "attention_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "total_ms": round(tot, 3),
+            "flops": flops}
+
+
 def configs_report(ca, synth, torch):
     """The other workloads, after the timed steps: the GQA prefill and the
     wide-head varlen prefill as full rings over every rank, and the pass-Q decode
@@ -324,12 +382,18 @@ def configs_report(ca, synth, torch):
     torch.cuda.empty_cache()
     mla = _decode_gbs(ca, torch, 8, 1 << 20, 8, 128, 1, 512)
     torch.cuda.empty_cache()
+    log("bench: Ulysses attention of the GQA prefill")
+    uly = _ulysses_gqa(ca, synth, torch, synth.WORKLOADS["gqa"])
+    torch.cuda.empty_cache()
     return {
         "gqa_prefill": dict(workload="S=32768, cp=8, 32q/8kv, d128, bf16; all 8 ranks x 8 steps", **gqa),
         "wide_varlen_prefill": dict(workload=f"6 packed sequences ({synth.WORKLOADS['varlen'].total_tokens} tokens), "
                                              "cp=4, 64 heads, d512, bf16; all 4 ranks x 4 steps", **wide),
         "mqa_decode": dict(workload="b=8, kv_len=1048576, cp=8, 32q/1kv, d128, bf16", **mqa),
         "mla_like_decode": dict(workload="b=8, kv_len=1048576, cp=8, 128q/1kv, d512, bf16", **mla),
+        "ulysses_gqa_prefill": dict(workload="S=32768, 32q/8kv, d128, bf16; Ulysses over u=8 ranks: all-to-all of "
+                                             "Q, K, V, per-rank attention over 4q/1kv heads, inverse all-to-all "
+                                             "of out and lse", **uly),
     }
 
 
@@ -343,7 +407,7 @@ def main():
                     help="skip the measurements of the other workloads that follow the timed steps")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the transfer/compute overlap measurements that follow the timed steps")
-    ap.add_argument("--config-only", choices=["gqa", "varlen", "mqa", "mla"], default=None,
+    ap.add_argument("--config-only", choices=["gqa", "varlen", "mqa", "mla", "ulysses"], default=None,
                     help="measure only this workload of the configs report (for profiling its kernels) and "
                          "print its JSON; no headline step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -366,6 +430,8 @@ def main():
     if args.config_only:
         if args.config_only in ("gqa", "varlen"):
             r = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS[args.config_only], reps=args.steps)
+        elif args.config_only == "ulysses":
+            r = _ulysses_gqa(ca, synth, torch, synth.WORKLOADS["gqa"], reps=args.steps)
         else:
             heads = {"mqa": (32, 128), "mla": (128, 512)}[args.config_only]
             r = _decode_gbs(ca, torch, 8, 1 << 20, 8, heads[0], 1, heads[1], reps=args.steps)
