@@ -138,3 +138,47 @@ def test_decode_workload_full_size_sampled():
     compare("reduced", out[bi, heads].cpu().numpy(), lse[bi, heads].cpu().numpy(), wo[0], wl[0], TOL_BF16)
     # every output is finite and every lse is a real number (all rows saw keys)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+def test_mla_like_decode_full_size_sampled():
+    """The MLA-like decode at the size the bench times: b = 8, kv_len = 1048576 in
+    cp = 8 shards, 128 query heads on one kv head, head_dim 512, bf16 (it runs
+    decode_wide). Sampled check: batch entry 3, query heads 5, 21, ..., 117 (one
+    in every 16-head block, so every wave of the workload's workgroups): the 8
+    shard partials and the reduced output against the oracle over the 1M keys.
+    The K/V slice of that batch entry is the shared input generator's output
+    (generated on the device, copied to the host)."""
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    b, S, cp, H, G, D = 8, 1 << 20, 8, 128, 1, 512
+    seed, scale_in = 23, 1.0
+    scale = D ** -0.5
+    log(f"[decode full] MLA-like b={b} kv_len={S} cp={cp} heads={H}/{G} d={D}")
+    n = S // cp
+    q = synth.tensor_torch(seed, synth.TENSOR_Q, (b, H, D), scale_in, "bf16", "cuda")
+    ks, vs, host = [], [], {}
+    bi = 3
+    for tid, lst in ((synth.TENSOR_K, ks), (synth.TENSOR_V, vs)):
+        full = synth.tensor_torch(seed, tid, (b * S, G, D), scale_in, "bf16", "cuda").view(b, S, G, D)
+        host[tid] = full[bi].view(torch.int16).cpu().numpy().view(np.uint16)[None]   # [1, S, 1, D] bf16 bits
+        for s in range(cp):
+            lst.append(full[:, s * n:(s + 1) * n].contiguous())
+        del full
+    torch.cuda.synchronize()
+    desc = ca.DecodeDesc(batch=b, cp=cp, kv_len=S, n_hq=H, n_kv=G, head_dim=D, dtype="bf16", scale=scale)
+    sp, out, lse = _run(ca, desc, q, ks, vs)
+    del ks, vs
+    heads = np.arange(5, H, 16)
+    qg = synth.tensor_np(seed, synth.TENSOR_Q, (b, H, D), scale_in, "bf16")[bi:bi + 1, heads]
+    log("  oracle: 8 query heads over the batch entry's 1M keys")
+    shards, wo, wl = oracle.passq_decode(qg, host[synth.TENSOR_K], host[synth.TENSOR_V], cp, scale)
+    m = sp.m.cpu().numpy().reshape(cp, b, H)
+    den = sp.den.cpu().numpy().reshape(cp, b, H)
+    num = sp.num.cpu().numpy().reshape(cp, b, H, D)
+    for s in range(cp):
+        go, gl = canonical_np(m[s, bi, heads], den[s, bi, heads], num[s, bi, heads])
+        so, sl = oracle.finalize(shards[s])
+        compare(f"shard {s}", go, gl, so[0], sl[0], TOL_BF16)
+    compare("reduced", out[bi, heads].cpu().numpy(), lse[bi, heads].cpu().numpy(), wo[0], wl[0], TOL_BF16)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()

@@ -128,3 +128,50 @@ def test_ulysses_and_hybrid_match_the_oracle(lens, u, c, n_hq, n_kv, d, dtype):
         for i in range(u):
             _check_rank(f"ring rank {r}, Ulysses rank {i}", out_s[i], lse_s[i], pos[r][i * R:(i + 1) * R],
                         ref_out, ref_lse, tol)
+
+
+def test_ulysses_gqa_workload_full_size_sampled():
+    """Ulysses over u = 8 ranks at the size the bench times: the GQA prefill
+    (S = 32768, 32q/8kv, d128, bf16), all-to-all, per-rank attention over 4q/1kv
+    heads, inverse all-to-all. Sampled check: 6 rows of every Ulysses rank (its
+    first, last and four between) x all 32 heads against the oracle's unsplit
+    attention over the whole sequence."""
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    import synth
+    w = synth.WORKLOADS["gqa"]
+    S, H, G, d, u = w.total_tokens, w.n_hq, w.n_kv, w.head_dim, 8
+    R = S // u
+    log(f"ulysses full size S={S} heads={H}/{G} d={d} u={u}")
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, "cuda")
+    seq = {n: [t[i * R:(i + 1) * R].contiguous() for i in range(u)] for n, t in (("q", q), ("k", k), ("v", v))}
+    head = {}
+    for n, nh in (("q", H), ("k", G), ("v", G)):
+        head[n] = [torch.empty(S, nh // u, d, dtype=q.dtype, device="cuda") for _ in range(u)]
+        ca.ulysses_all_to_all(seq[n], head[n], nh, "seq_to_head")
+    desc = ca.PrefillDesc(cp=1, cu_seqlens=w.cu_seqlens, n_hq=H // u, n_kv=G // u, head_dim=d, dtype=w.dtype,
+                          scale=w.softmax_scale)
+    out_h, lse_h = [], []
+    for i in range(u):
+        acc = ca.new_partial(S, H // u, d)
+        ca.ring_step_partial(desc, 0, 0, head["q"][i], head["k"][i], head["v"][i], acc, accumulate=False)
+        out_h.append(torch.empty(S, H // u, d, device="cuda"))
+        lse_h.append(torch.empty(S, H // u, device="cuda"))
+        ca.merge(acc, [], out=out_h[i], lse=lse_h[i])
+    out_s = [torch.empty(R, H, d, device="cuda") for _ in range(u)]
+    lse_s = [torch.empty(R, H, device="cuda") for _ in range(u)]
+    ca.ulysses_all_to_all(out_h, out_s, H, "head_to_seq")
+    ca.ulysses_all_to_all(lse_h, lse_s, H, "head_to_seq")
+    torch.cuda.synchronize()
+    kn = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vn = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for i in range(u):
+        local = np.unique(np.linspace(0, R - 1, 6).astype(np.int64))
+        pos = i * R + local
+        qr = q[torch.from_numpy(pos).to("cuda")].view(torch.int16).cpu().numpy().view(np.uint16)
+        ro, rl = oracle.attention_reference_rows(qr, pos, kn, vn, w.softmax_scale)
+        compare(f"Ulysses rank {i}", out_s[i][torch.from_numpy(local).to("cuda")].cpu().numpy(),
+                lse_s[i][torch.from_numpy(local).to("cuda")].cpu().numpy(), ro, rl, TOL_BF16)
