@@ -2,7 +2,8 @@
 hand-picked cases: head_dim 64/128/512, 1 to 4 kv heads with 1 to 32 query
 heads each, cp from 1 to 8, 1 to 4 packed sequences of any admissible length
 (with empty ones), the plain and the padded layout, bf16 and fp32; and pass-Q
-decode over batch, shard count, group size and head_dim. Every configuration
+decode over batch, shard count, group size and head_dim (plus a set at head_dim
+512 with 120 to 256 query heads per kv head). Every configuration
 runs the whole fused ring of every rank (or the decode) through the C-ABI and
 is compared with the fp64 oracle on every real row. The draw is deterministic,
 so a failure names a reproducible case."""
@@ -62,8 +63,25 @@ def _decode_cases(n, seed=2025):
     return out
 
 
+def _wide_decode_cases(n, seed=2026):
+    """head_dim 512 with more than 112 query heads per kv head (the 128-head
+    workgroups of the MLA-like layouts), bf16: full and partly filled head
+    blocks, several kv heads, shards shorter than a 32-key tile."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        n_kv = int(g.choice([1, 2, 3]))
+        rep = int(g.choice([120, 128, 136, 160, 192, 256]))
+        cp = int(g.choice([1, 2, 3, 4, 8]))
+        b = int(g.integers(1, 4))
+        S = cp * int(g.integers(1, 400 // cp + 1))
+        out.append((f"w{len(out):02d}-D512-h{n_kv * rep}x{n_kv}-cp{cp}-b{b}-S{S}-bf16", b, S, cp, n_kv * rep, n_kv,
+                    512, "bf16"))
+    return out
+
+
 PREFILL = _prefill_cases(48)
-DECODE = _decode_cases(32)
+DECODE = _decode_cases(32) + _wide_decode_cases(12)
 
 
 def _padded_locals(ca, cu, cp, tensors):
