@@ -228,7 +228,10 @@ def overlap_report(ca, synth, torch):
 def _full_ring_tflops(ca, synth, torch, w, reps=3):
     """Every rank's full ring (cp fused ring steps per rank, then finalize) of a
     prefill workload: exact causal FLOPs of all cp^2 ring-step launches / their
-    summed HIP-event time on the launch stream (median over reps)."""
+    HIP-event time on the launch stream, one event pair around each rank's cp
+    back-to-back launches (the finalize between ranks is outside), summed over
+    the ranks (median over reps). One more pass with an event pair around every
+    launch gives the per-call figures."""
     S, cp, H, G, d = w.total_tokens, w.cp, w.n_hq, w.n_kv, w.head_dim
     cu = w.cu_seqlens
     q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
@@ -245,32 +248,36 @@ def _full_ring_tflops(ca, synth, torch, w, reps=3):
     out = torch.empty(rows, H, d, device="cuda")
     lse = torch.empty(rows, H, device="cuda")
     stream = torch.cuda.current_stream()
-    flops = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)["rank_flops_exact"] * cp
     exact = ca.account(cp=cp, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)
-    totals, per_call = [], []
-    for rep_i in range(reps + 1):
+    flops = exact["rank_flops_exact"] * cp
+
+    def ring(per_call):
         evs = []
         for r in range(cp):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
             for t in range(cp):
                 j = (r - t) % cp
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
                 ca.ring_step_partial(desc, r, t, loc[r][0], loc[j][1], loc[j][2], acc, accumulate=t > 0)
-                e1.record(stream)
-                evs.append((e0, e1))
+                if per_call or t == cp - 1:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    evs.append((e0, e1))
+                    e0 = e1
             ca.merge(acc, [], out=out, lse=lse)
         torch.cuda.synchronize()
-        if rep_i:
-            times = [a.elapsed_time(b) for a, b in evs]
-            totals.append(sum(times))
-            # per (rank, step): exact FLOPs of the call (step 0 holds the diagonal triangles)
-            per_call.append([(exact["step0_flops_exact"] if i % cp == 0 else exact["stepN_flops_exact"]) / (x * 1e-3) / 1e12
-                             for i, x in enumerate(times)])
+        return [a.elapsed_time(b) for a, b in evs]
+
+    ring(False)                     # warm-up
+    totals = [sum(ring(False)) for _ in range(reps)]
+    times = ring(True)              # per (rank, step); step 0 holds the diagonal triangles
+    calls = np.array([(exact["step0_flops_exact"] if i % cp == 0 else exact["stepN_flops_exact"]) / (x * 1e-3) / 1e12
+                      for i, x in enumerate(times)])
     ms = float(np.median(totals))
-    calls = np.median(np.array(per_call), axis=0)
     del loc
     return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "ring_ms": round(ms, 3), "launches": cp * cp, "flops": flops,
+            "per_launch_events_ms": round(float(sum(times)), 3),
             "per_call_tflops": {"min": round(float(calls.min()), 1), "median": round(float(np.median(calls)), 1),
                                 "max": round(float(calls.max()), 1)}}
 
