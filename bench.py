@@ -373,11 +373,87 @@ def _ulysses_gqa(ca, synth, torch, w, u=8, reps=3):
             "flops": flops}
 
 
+def _hybrid_gqa(ca, synth, torch, w, u=2, c=4, reps=3):
+    """Hybrid CP of a prefill workload, u Ulysses ranks inside each of c ring
+    ranks (cp = u c), emulated on the GPU: ring rank j holds the balanced
+    split's rows of rank j over c ranks and its u Ulysses ranks consecutive
+    slices of them; the all-to-all inside each ring group gives every Ulysses
+    rank all L = S/c rows of its ring rank for n_hq/u query and n_kv/u kv heads;
+    the pass-KV ring runs over the c ring ranks on each head group (c fused ring
+    steps per (ring rank, head group), then finalize); the inverse all-to-all
+    returns out and lse to the token slices. Reported: the all-to-alls' HBM
+    throughput (every byte read once and written once) and the rings' TFLOP/s
+    (exact causal FLOPs over the HIP-event time of each (ring rank, head group)'s
+    c back-to-back launches, summed); median over reps."""
+    S, H, G, d = w.total_tokens, w.n_hq, w.n_kv, w.head_dim
+    cu = w.cu_seqlens
+    pos = [ca.balanced_split(cu, c, j)[0] for j in range(c)]
+    L = len(pos[0])
+    R = L // u
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, "cuda")
+    idx = [torch.from_numpy(p).to("cuda") for p in pos]
+    seq = {n: [[t.index_select(0, idx[j][i * R:(i + 1) * R]).contiguous() for i in range(u)] for j in range(c)]
+           for n, t in (("q", q), ("k", k), ("v", v))}
+    del q, k, v, idx
+    head = {n: [[torch.empty(L, nh // u, d, dtype=seq[n][0][0].dtype, device="cuda") for _ in range(u)]
+                for _ in range(c)] for n, nh in (("q", H), ("k", G), ("v", G))}
+    desc = ca.PrefillDesc(cp=c, cu_seqlens=cu, n_hq=H // u, n_kv=G // u, head_dim=d, dtype=w.dtype,
+                          scale=w.softmax_scale)
+    acc = [[ca.new_partial(L, H // u, d) for _ in range(u)] for _ in range(c)]
+    out_h = [[torch.empty(L, H // u, d, device="cuda") for _ in range(u)] for _ in range(c)]
+    lse_h = [[torch.empty(L, H // u, device="cuda") for _ in range(u)] for _ in range(c)]
+    out_s = [[torch.empty(R, H, d, device="cuda") for _ in range(u)] for _ in range(c)]
+    lse_s = [[torch.empty(R, H, device="cuda") for _ in range(u)] for _ in range(c)]
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a2a_ms, ring_ms, tot_ms = [], [], []
+    for rep_i in range(reps + 1):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record(stream)
+        for j in range(c):
+            for n, nh in (("q", H), ("k", G), ("v", G)):
+                ca.ulysses_all_to_all(seq[n][j], head[n][j], nh, "seq_to_head")
+        e1.record(stream)
+        rings = []
+        for r in range(c):
+            for i in range(u):
+                a, b = ev(), ev()
+                a.record(stream)
+                for t in range(c):
+                    j = (r - t) % c
+                    ca.ring_step_partial(desc, r, t, head["q"][r][i], head["k"][j][i], head["v"][j][i], acc[r][i],
+                                         accumulate=t > 0)
+                b.record(stream)
+                rings.append((a, b))
+                ca.merge(acc[r][i], [], out=out_h[r][i], lse=lse_h[r][i])
+        e2.record(stream)
+        for j in range(c):
+            ca.ulysses_all_to_all(out_h[j], out_s[j], H, "head_to_seq")
+            ca.ulysses_all_to_all(lse_h[j], lse_s[j], H, "head_to_seq")
+        e3.record(stream)
+        torch.cuda.synchronize()
+        if rep_i:
+            a2a_ms.append(e0.elapsed_time(e1) + e2.elapsed_time(e3))
+            ring_ms.append(sum(x.elapsed_time(y) for x, y in rings))
+            tot_ms.append(e0.elapsed_time(e3))
+    a2a_bytes = 2 * (S * (H + 2 * G) * d * 2 + S * H * (d + 1) * 4)
+    flops = ca.account(cp=c, n_hq=H, n_kv=G, head_dim=d, dtype_bytes=2, cu_seqlens=cu)["rank_flops_exact"] * c
+    a, t, tot = float(np.median(a2a_ms)), float(np.median(ring_ms)), float(np.median(tot_ms))
+    return {"u": u, "c": c, "all_to_all_ms": round(a, 3), "all_to_all_gb_per_s": round(a2a_bytes / (a * 1e-3) / 1e9, 1),
+            "all_to_all_frac": round(a2a_bytes / (a * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "all_to_all_bytes": a2a_bytes,
+            "ring_ms": round(t, 3), "ring_tflops": round(flops / (t * 1e-3) / 1e12, 1),
+            "ring_frac": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "launches": u * c * c,
+            "total_ms": round(tot, 3), "flops": flops}
+
+
 def configs_report(ca, synth, torch):
     """The other workloads, after the timed steps: the GQA prefill and the
-    wide-head varlen prefill as full rings over every rank, and the pass-Q decode
+    wide-head varlen prefill as full rings over every rank, the pass-Q decode
     with one kv head (MQA 32/1 at head_dim 128; MLA-like 128/1 at head_dim 512;
-    b = 8, kv_len = 1048576, cp = 8, K/V ~ N(0,1))."""
+    b = 8, kv_len = 1048576, cp = 8, K/V ~ N(0,1)), and the GQA prefill under
+    Ulysses (u = 8) and hybrid CP (u = 2 inside c = 4 ring ranks)."""
     log("bench: GQA prefill, full ring")
     gqa = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS["gqa"])
     torch.cuda.empty_cache()
@@ -392,6 +468,9 @@ def configs_report(ca, synth, torch):
     log("bench: Ulysses attention of the GQA prefill")
     uly = _ulysses_gqa(ca, synth, torch, synth.WORKLOADS["gqa"])
     torch.cuda.empty_cache()
+    log("bench: hybrid CP of the GQA prefill")
+    hyb = _hybrid_gqa(ca, synth, torch, synth.WORKLOADS["gqa"])
+    torch.cuda.empty_cache()
     return {
         "gqa_prefill": dict(workload="S=32768, cp=8, 32q/8kv, d128, bf16; all 8 ranks x 8 steps", **gqa),
         "wide_varlen_prefill": dict(workload=f"6 packed sequences ({synth.WORKLOADS['varlen'].total_tokens} tokens), "
@@ -401,6 +480,9 @@ def configs_report(ca, synth, torch):
         "ulysses_gqa_prefill": dict(workload="S=32768, 32q/8kv, d128, bf16; Ulysses over u=8 ranks: all-to-all of "
                                              "Q, K, V, per-rank attention over 4q/1kv heads, inverse all-to-all "
                                              "of out and lse", **uly),
+        "hybrid_gqa_prefill": dict(workload="S=32768, 32q/8kv, d128, bf16; hybrid CP, u=2 Ulysses ranks inside each "
+                                            "of c=4 ring ranks: all-to-all inside ring groups, pass-KV ring over "
+                                            "the ring ranks per head group (16q/4kv), inverse all-to-all", **hyb),
     }
 
 
@@ -414,7 +496,7 @@ def main():
                     help="skip the measurements of the other workloads that follow the timed steps")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the transfer/compute overlap measurements that follow the timed steps")
-    ap.add_argument("--config-only", choices=["gqa", "varlen", "mqa", "mla", "ulysses"], default=None,
+    ap.add_argument("--config-only", choices=["gqa", "varlen", "mqa", "mla", "ulysses", "hybrid"], default=None,
                     help="measure only this workload of the configs report (for profiling its kernels) and "
                          "print its JSON; no headline step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -439,6 +521,8 @@ def main():
             r = _full_ring_tflops(ca, synth, torch, synth.WORKLOADS[args.config_only], reps=args.steps)
         elif args.config_only == "ulysses":
             r = _ulysses_gqa(ca, synth, torch, synth.WORKLOADS["gqa"], reps=args.steps)
+        elif args.config_only == "hybrid":
+            r = _hybrid_gqa(ca, synth, torch, synth.WORKLOADS["gqa"], reps=args.steps)
         else:
             heads = {"mqa": (32, 128), "mla": (128, 512)}[args.config_only]
             r = _decode_gbs(ca, torch, 8, 1 << 20, 8, heads[0], 1, heads[1], reps=args.steps)

@@ -175,3 +175,63 @@ def test_ulysses_gqa_workload_full_size_sampled():
         ro, rl = oracle.attention_reference_rows(qr, pos, kn, vn, w.softmax_scale)
         compare(f"Ulysses rank {i}", out_s[i][torch.from_numpy(local).to("cuda")].cpu().numpy(),
                 lse_s[i][torch.from_numpy(local).to("cuda")].cpu().numpy(), ro, rl, TOL_BF16)
+
+
+def test_hybrid_gqa_workload_full_size_sampled():
+    """Hybrid CP at the size the bench times: the GQA prefill (S = 32768,
+    32q/8kv, d128, bf16), u = 2 Ulysses ranks inside each of c = 4 ring ranks:
+    all-to-all inside each ring group, the pass-KV ring over the 4 ring ranks on
+    each 16q/4kv head group, inverse all-to-all. Sampled check: 6 rows of every
+    (ring rank, Ulysses rank) (its first, last and four between) x all 32 heads
+    against the oracle's unsplit attention over the whole sequence."""
+    need_gpu()
+    import torch
+    import context_attention_amd as ca
+    import synth
+    w = synth.WORKLOADS["gqa"]
+    S, H, G, d, u, c = w.total_tokens, w.n_hq, w.n_kv, w.head_dim, 2, 4
+    log(f"hybrid full size S={S} heads={H}/{G} d={d} u={u} c={c}")
+    pos = [ca.balanced_split(w.cu_seqlens, c, j)[0] for j in range(c)]
+    L = len(pos[0])
+    R = L // u
+    q = synth.tensor_torch(w.seed, synth.TENSOR_Q, (S, H, d), w.scale_in, w.dtype, "cuda")
+    k = synth.tensor_torch(w.seed, synth.TENSOR_K, (S, G, d), w.scale_in, w.dtype, "cuda")
+    v = synth.tensor_torch(w.seed, synth.TENSOR_V, (S, G, d), w.scale_in, w.dtype, "cuda")
+    idx = [torch.from_numpy(p).to("cuda") for p in pos]
+    seq = {n: [[t.index_select(0, idx[j][i * R:(i + 1) * R]).contiguous() for i in range(u)] for j in range(c)]
+           for n, t in (("q", q), ("k", k), ("v", v))}
+    head = {}
+    for n, nh in (("q", H), ("k", G), ("v", G)):
+        head[n] = []
+        for j in range(c):
+            dst = [torch.empty(L, nh // u, d, dtype=q.dtype, device="cuda") for _ in range(u)]
+            ca.ulysses_all_to_all(seq[n][j], dst, nh, "seq_to_head")
+            head[n].append(dst)
+    desc = ca.PrefillDesc(cp=c, cu_seqlens=w.cu_seqlens, n_hq=H // u, n_kv=G // u, head_dim=d, dtype=w.dtype,
+                          scale=w.softmax_scale)
+    kn = k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vn = v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(c):
+        out_h, lse_h = [], []
+        for i in range(u):
+            acc = ca.new_partial(L, H // u, d)
+            for t in range(c):
+                j = (r - t) % c
+                ca.ring_step_partial(desc, r, t, head["q"][r][i], head["k"][j][i], head["v"][j][i], acc,
+                                     accumulate=t > 0)
+            out_h.append(torch.empty(L, H // u, d, device="cuda"))
+            lse_h.append(torch.empty(L, H // u, device="cuda"))
+            ca.merge(acc, [], out=out_h[i], lse=lse_h[i])
+        out_s = [torch.empty(R, H, d, device="cuda") for _ in range(u)]
+        lse_s = [torch.empty(R, H, device="cuda") for _ in range(u)]
+        ca.ulysses_all_to_all(out_h, out_s, H, "head_to_seq")
+        ca.ulysses_all_to_all(lse_h, lse_s, H, "head_to_seq")
+        torch.cuda.synchronize()
+        for i in range(u):
+            local = np.unique(np.linspace(0, R - 1, 6).astype(np.int64))
+            gpos = pos[r][i * R + local]
+            qr = q[torch.from_numpy(gpos).to("cuda")].view(torch.int16).cpu().numpy().view(np.uint16)
+            ro, rl = oracle.attention_reference_rows(qr, gpos, kn, vn, w.softmax_scale)
+            sel = torch.from_numpy(local).to("cuda")
+            compare(f"ring rank {r}, Ulysses rank {i}", out_s[i][sel].cpu().numpy(), lse_s[i][sel].cpu().numpy(),
+                    ro, rl, TOL_BF16)
