@@ -76,8 +76,33 @@ CASES = [
 ]
 
 
+def _random_cases(n, seed=77):
+    """Seeded random Ulysses (c = 1) and hybrid shapes: u in {1, 2, 4, 8}, c in
+    {1, 2, 3, 4}, GQA ratios 1-8 with u dividing the kv heads, d 64/128/512, bf16
+    and fp32, one to three packed sequences whose lengths are multiples of 2c,
+    and a ring rank's rows a multiple of u."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        u = int(g.choice([1, 2, 4, 8]))
+        c = int(g.choice([1, 2, 3, 4]))
+        n_kv = u * int(g.choice([1, 2]))
+        n_hq = n_kv * int(g.choice([1, 2, 4, 8]))
+        d = int(g.choice([64, 128, 512]))
+        dtype = "f32" if g.random() < 0.25 else "bf16"
+        nseq = int(g.integers(1, 4))
+        lens = [2 * c * int(g.integers(1, 1200 // (2 * c * nseq) + 2)) for _ in range(nseq)]
+        if (sum(lens) // c) % u or n_hq * d * sum(lens) > 6_000_000:
+            continue
+        out.append((lens, u, c, n_hq, n_kv, d, dtype))
+    return out
+
+
+CASES = CASES + _random_cases(10)
+
+
 @pytest.mark.parametrize("lens,u,c,n_hq,n_kv,d,dtype", CASES,
-                         ids=[f"u{x[1]}-c{x[2]}-{x[6]}-d{x[5]}-{len(x[0])}seq" for x in CASES])
+                         ids=[f"u{x[1]}-c{x[2]}-{x[6]}-d{x[5]}-h{x[3]}x{x[4]}-S{sum(x[0])}-{len(x[0])}seq" for x in CASES])
 def test_ulysses_and_hybrid_match_the_oracle(lens, u, c, n_hq, n_kv, d, dtype):
     need_gpu()
     import torch
