@@ -24,8 +24,9 @@
  *     only. Device pointers must stay valid until the work enqueued on the
  *     given stream has finished; the library keeps no pointer after it
  *     returns, allocates no memory (device or host) and creates no HIP
- *     object (streams and events are the caller's), and has no global state.
- *     Calls are reentrant. Faults of enqueued kernels surface at the caller's next
+ *     object (streams and events are the caller's), and has no global state
+ *     (one exception: the per-GPU scratch buffer of
+ *     cpattn_passq_decode_noalloc, below). Calls are reentrant. Faults of enqueued kernels surface at the caller's next
  *     synchronisation.
  *   - There are no defaults: cp, scale and the shapes are explicit (the
  *     spec's interface appendix: cp is an explicit positive integer, a
