@@ -1,7 +1,8 @@
 """GPU parity over shapes drawn at random from a fixed seed, beside the
 hand-picked cases: head_dim 64/128/512, 1 to 4 kv heads with 1 to 32 query
 heads each, cp from 1 to 8, 1 to 4 packed sequences of any admissible length
-(with empty ones), the plain and the padded layout, bf16 and fp32; and pass-Q
+(with empty ones), the plain and the padded layout, bf16 and fp32, plus query
+heads per kv head that are not powers of two (3, 5, 6, 12); and pass-Q
 decode over batch, shard count, group size and head_dim (plus a set at head_dim
 512 with 120 to 256 query heads per kv head). Every configuration
 runs the whole fused ring of every rank (or the decode) through the C-ABI and
@@ -80,7 +81,34 @@ def _wide_decode_cases(n, seed=2026):
     return out
 
 
-PREFILL = _prefill_cases(48)
+def _odd_group_cases(n, seed=2027):
+    """Prefill with query heads per kv head that are not powers of two (3, 5,
+    6, 12: head groups of 1, 2 and 4 heads per workgroup, head-group counts
+    that are not multiples of 8, so the unit-major workgroup order) and 1 to 3
+    kv heads."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(g.choice([64, 128, 512], p=[0.4, 0.4, 0.2]))
+        n_kv = int(g.choice([1, 2, 3]))
+        rep = int(g.choice([3, 5, 6, 12]))
+        if d == 512 and n_kv * rep > 16:
+            continue
+        cp = int(g.choice([1, 2, 3, 4, 8]))
+        dtype = "f32" if g.random() < 0.15 else "bf16"
+        padded = bool(g.random() < 0.3)
+        ns = int(g.integers(1, 4))
+        cap = 900 if d < 512 else 400
+        if padded:
+            lens = [int(x) for x in g.integers(1, cap // ns + 1, ns)]
+        else:
+            lens = [2 * cp * int(x) for x in g.integers(1, cap // (2 * cp * ns) + 2, ns)]
+        name = f"o{len(out):02d}-d{d}-h{n_kv * rep}x{n_kv}-cp{cp}-{dtype}-{'pad' if padded else 'exact'}-{ns}seq"
+        out.append((name, lens, cp, n_kv * rep, n_kv, d, dtype, padded))
+    return out
+
+
+PREFILL = _prefill_cases(48) + _odd_group_cases(10)
 DECODE = _decode_cases(32) + _wide_decode_cases(12)
 
 
