@@ -660,6 +660,7 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   const bool row_in = row < c;          // a row of the local buffer
   const bool row_ok = row < q_valid;    // a real (non-pad) row
   const int64_t grow = qrow0 + row;
+  const bool wave_idle = wrow0 >= q_valid;   // every row of the wave is a pad row (or past the chunk)
 
   if (nseg == 0) {
     float *mptr = a.m + (grow * a.n_hq + h);
@@ -836,9 +837,30 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
       vf = nv;
     }
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    tile_step(it, 0);
-    if (it + 1 < ntiles) tile_step(it + 1, 1);
+  if (wave_idle) {
+    // no row of this wave is real: its outputs are the identity whatever the
+    // keys, so it only keeps the workgroup's copy and barrier schedule, one
+    // tile at a time (the same waits, barriers and copies as tile_step)
+    for (int it = 0; it < ntiles; ++it) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+      const int nxt = (it & 1) ^ 1;
+#pragma unroll
+      for (int i = 0; i < KS / 2; ++i) {
+        const int q = wv + NW * (i % CPW);
+        if (i < CPW)
+          dma_1k((i & 1) ? koff1 : koff0, uniform_words(kw.row(q, row_bytes, gbase)), Ks[nxt] + q * 512);
+        else
+          dma_1k(voff, uniform_words(vw.row(q, row_bytes, gbase)), Vt[nxt] + q * 512);
+      }
+      kw.next();
+      vw.next();
+    }
+  } else {
+    for (int it = 0; it < ntiles; it += 2) {
+      tile_step(it, 0);
+      if (it + 1 < ntiles) tile_step(it + 1, 1);
+    }
   }
   // the copies issued past the last tile (empty ranges: zeros, no memory read)
   // land before the workgroup's LDS is released
