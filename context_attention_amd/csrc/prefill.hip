@@ -565,30 +565,38 @@ void ring_step_mfma(SeqTable tab, StepArgs a) {
     float *dptr = a.den + (grow[nb] * a.n_hq + h);
     float *nptr = a.num + (grow[nb] * a.n_hq + h) * (int64_t)D;
     const float m_nat = (m_ref[nb] == kNegInf || !row_ok[nb]) ? kNegInf : m_ref[nb] * a.scale;
-    float w_old = 0.f, w_new = 1.f, m_out = m_nat;
+    auto out_at = [&](int db, int g4) {
+      const f32x4_t o = {oacc[nb][db][4 * g4], oacc[nb][db][4 * g4 + 1], oacc[nb][db][4 * g4 + 2],
+                         oacc[nb][db][4 * g4 + 3]};
+      return row_ok[nb] ? o : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
     if (a.accumulate) {
+      // every load of the previous triple is issued before the first use, so
+      // the row's accumulator read costs one memory latency, not one per load
       const float m_old = *mptr;
-      merge_weights(m_old, m_nat, m_out, w_old, w_new);
       const float d_old = *dptr;
-      const float d_out = w_old * d_old + w_new * l_tot;
-      if (hf == 0) store_stats(mptr, dptr, m_out, d_out);
+      f32x4_t old[DB][4];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          old[db][g4] = *reinterpret_cast<const f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf);
+      float w_old, w_new, m_out;
+      merge_weights(m_old, m_nat, m_out, w_old, w_new);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = old[db][g4] * w_old + out_at(db, g4) * w_new;
+      if (hf == 0) store_stats(mptr, dptr, m_out, w_old * d_old + w_new * l_tot);
     } else {
       if (hf == 0) store_stats(mptr, dptr, m_nat, l_tot);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4_t *>(nptr + db * 32 + 8 * g4 + 4 * hf) = out_at(db, g4);
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float *p = nptr + db * 32 + 8 * g4 + 4 * hf;
-        f32x4_t o = {oacc[nb][db][4 * g4], oacc[nb][db][4 * g4 + 1], oacc[nb][db][4 * g4 + 2],
-                     oacc[nb][db][4 * g4 + 3]};
-        if (!row_ok[nb]) o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (a.accumulate) {
-          const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
-          o = old * w_old + o * w_new;
-        }
-        *reinterpret_cast<f32x4_t *>(p) = o;
-      }
   }
 }
 
@@ -878,24 +886,38 @@ void ring_step_wide(SeqTable tab, StepArgs a) {
   float *dptr = a.den + ri;
   float *nptr = a.num + ri * (int64_t)D;
   const float m_nat = (m_ref == kNegInf || !row_ok) ? kNegInf : m_ref * a.scale;
-  float w_old = 0.f, w_new = 1.f;
   if (a.accumulate) {
-    float m_out;
-    merge_weights(*mptr, m_nat, m_out, w_old, w_new);
-    const float d_out = w_old * (*dptr) + w_new * l_tot;
-    if (grp == 0) store_stats(mptr, dptr, m_out, d_out);
-  } else if (grp == 0) {
-    store_stats(mptr, dptr, m_nat, l_tot);
-  }
+    // the previous triple is read in groups of kEpiBlocks 16-column blocks,
+    // every load of a group issued before the group's first use; the stats go
+    // last so that no load waits behind a store the compiler cannot tell apart
+    const float m_old = *mptr;
+    const float d_old = *dptr;
+    constexpr int kEpiBlocks = 8;
+    static_assert(DB % kEpiBlocks == 0, "whole groups of output blocks");
+    f32x4_t old[kEpiBlocks];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    float *p = nptr + 16 * db + 4 * grp;
-    f32x4_t o = row_ok ? oacc[db] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (a.accumulate) {
-      const f32x4_t old = *reinterpret_cast<const f32x4_t *>(p);
-      o = old * w_old + o * w_new;
+    for (int i = 0; i < kEpiBlocks; ++i) old[i] = *reinterpret_cast<const f32x4_t *>(nptr + 16 * i + 4 * grp);
+    float w_old, w_new, m_out;
+    merge_weights(m_old, m_nat, m_out, w_old, w_new);
+#pragma unroll
+    for (int g0 = 0; g0 < DB; g0 += kEpiBlocks) {
+      if (g0 > 0) {
+#pragma unroll
+        for (int i = 0; i < kEpiBlocks; ++i)
+          old[i] = *reinterpret_cast<const f32x4_t *>(nptr + 16 * (g0 + i) + 4 * grp);
+      }
+#pragma unroll
+      for (int i = 0; i < kEpiBlocks; ++i) {
+        const f32x4_t o = row_ok ? oacc[g0 + i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4_t *>(nptr + 16 * (g0 + i) + 4 * grp) = old[i] * w_old + o * w_new;
+      }
     }
-    *reinterpret_cast<f32x4_t *>(p) = o;
+    if (grp == 0) store_stats(mptr, dptr, m_out, w_old * d_old + w_new * l_tot);
+  } else {
+    if (grp == 0) store_stats(mptr, dptr, m_nat, l_tot);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4_t *>(nptr + 16 * db + 4 * grp) = row_ok ? oacc[db] : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 }
 
